@@ -1,0 +1,224 @@
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+A step is one pass of the whole path over the mixed continuous-batching
+workload (4 chunked-prefill sequences of 512 new tokens at offsets up to 8192,
+200 decode sequences with contexts of 1024..32768 tokens, 50 of them sharing a
+4096-token prefix, 32/8 heads, head_dim 128, block 256, bf16):
+
+    kv_store of all 2248 new tokens -> causal paged prefill -> split-K decode (+ reduce)
+
+on one stream, inputs resident in HBM.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload 5] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, kc, vc, budget_s: float = 12.0):
+    """The fp64 oracle timed on a bounded sample of the decode part of the workload:
+    whole sequences, in order, until the time budget is spent.  Returns KV GB/s."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+
+    t0 = time.perf_counter()
+    done_bytes = 0
+    n = 0
+    row = 2 * w.num_kv_heads * w.head_dim * w.elt_bytes
+    while n < len(w.dec_context_lens) and time.perf_counter() - t0 < budget_s:
+        oracle.decode(w.dec_q[n:n + 1], kc, vc, w.dec_block_tables[n:n + 1], w.dec_context_lens[n:n + 1], w.scale,
+                      w.dtype, w.block_size)
+        done_bytes += int(w.dec_context_lens[n]) * row
+        n += 1
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {
+        "value": round(done_bytes / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"fp64 numpy oracle decode of the first {n} of {len(w.dec_context_lens)} decode sequences "
+                  f"({done_bytes / 1e9:.3f} GB of K/V, {dt:.1f} s), same algorithmic bytes per token as the GPU figure",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=5, help="workload number (5 = the mixed step)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--split-tokens", type=int, default=0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_gqa_mapping_amd as pkv
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    pkv.lib()  # fail loudly if the library is missing
+
+    t_build = time.perf_counter()
+    w = W.make_config(args.workload)
+    log(f"built workload {w.name} on the host in {time.perf_counter() - t_build:.1f} s")
+
+    def dev(a, bf=False):
+        if a is None:
+            return None
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16) if bf else torch.from_numpy(
+            np.ascontiguousarray(a))
+        return t.cuda()
+
+    bf = w.dtype == W.BF16
+    kc, vc = dev(w.k_cache, bf), dev(w.v_cache, bf)
+    nk, nv, slots = dev(w.new_k, bf), dev(w.new_v, bf), dev(w.slot_mapping)
+    has_dec, has_pre = w.dec_q is not None, w.pre_q is not None
+    if has_dec:
+        dq, dbt, dcl = dev(w.dec_q, bf), dev(w.dec_block_tables), dev(w.dec_context_lens)
+        dout = torch.empty_like(dq)
+        B, Hq, D = dq.shape
+        split = args.split_tokens or pkv.decode_split_tokens(B, Hq, w.num_kv_heads, D, w.max_context_len,
+                                                             w.block_size, 1 if bf else 0)
+        ws_bytes = pkv.decode_workspace_bytes(B, Hq, D, w.max_context_len, split)
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    if has_pre:
+        pq, pbt, cuq, cuk = dev(w.pre_q, bf), dev(w.pre_block_tables), dev(w.cu_seqlens_q), dev(w.cu_seqlens_k)
+        pout = torch.empty_like(pq)
+    torch.cuda.synchronize()
+    log("inputs resident on the GPU")
+
+    n_ev = 5
+    def step(events=None):
+        def rec(i):
+            if events is not None:
+                events[i].record()
+        rec(0)
+        pkv.kv_store(nk, nv, kc, vc, slots)
+        rec(1)
+        if has_pre:
+            pkv.paged_prefill_attn(pq, kc, vc, cuq, cuk, pbt, pout, max_seqlen_q=w.max_seqlen_q,
+                                   max_seqlen_k=w.max_seqlen_k, scale=w.scale)
+        rec(2)
+        if has_dec:
+            pkv.paged_decode_split(dq, kc, vc, dbt, dcl, w.scale, dout, max_context_len=w.max_context_len,
+                                   split_tokens=split, workspace=ws)
+            rec(3)
+            pkv.paged_decode_reduce(dq, kc, vc, dbt, dcl, w.scale, dout, max_context_len=w.max_context_len,
+                                    split_tokens=split, workspace=ws)
+        else:
+            rec(3)
+        rec(4)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    def avg(i, j):
+        return float(np.mean([e[i].elapsed_time(e[j]) for e in evs]))  # ms
+
+    t_store, t_pre, t_split, t_red = avg(0, 1), avg(1, 2), avg(2, 3), avg(3, 4)
+    kv_bytes = w.decode_kv_bytes()
+    dec_io = w.decode_io_bytes()
+    flops = w.prefill_flops()
+    store_bytes = w.store_bytes()
+    split_bytes = kv_bytes + dec_io
+    achieved_gbs = split_bytes / (t_split * 1e-3) / 1e9 if has_dec else 0.0
+
+    kernels = {
+        "kv_store": {"ms": round(t_store, 5), "GB/s": round(store_bytes / (t_store * 1e-3) / 1e9, 1),
+                     "tokens": int(len(w.slot_mapping))},
+        "decode_split": {"ms": round(t_split, 5), "GB/s": round(achieved_gbs, 1),
+                         "frac_hbm": round(achieved_gbs / HBM_PEAK_GBS, 4), "split_tokens": int(split) if has_dec else 0},
+        "decode_reduce": {"ms": round(t_red, 5)},
+    }
+    if has_pre:
+        tfs = flops / (t_pre * 1e-3) / 1e12
+        kernels["prefill"] = {"ms": round(t_pre, 5), "TFLOP/s": round(tfs, 2),
+                              "frac_mfma": round(tfs / MFMA_BF16_PEAK_TFS, 4), "tflop": round(flops / 1e12, 5)}
+    if has_dec:
+        value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "row_attn_kernel (decode split pass)",
+                    "algorithmic_bytes_per_launch": int(split_bytes)}
+    else:
+        value = flops / (ms_per_step * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(kernels["prefill"]["TFLOP/s"], 2), "peak": MFMA_BF16_PEAK_TFS,
+                    "unit": "TFLOP/s", "frac": kernels["prefill"]["frac_mfma"], "traffic": None,
+                    "kernel": "prefill_mfma_kernel"}
+
+    cpu = None
+    if not args.no_cpu_baseline and has_dec:
+        log("timing the oracle on a bounded sample")
+        import oracle
+
+        okc, ovc = oracle.kv_store(w.k_cache, w.v_cache, w.new_k, w.new_v, w.slot_mapping, w.block_size)
+        cpu = cpu_baseline(w, okc, ovc)
+
+    out = {
+        "metric": "paged decode attn KV GB/s & % HBM peak; prefill attn TFLOP/s & % MFMA peak",
+        "value": round(value, 2),
+        "unit": "GB/s" if has_dec else "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf else "f32",
+        "data": "synthetic (seeded N(0,1) values, seeded lengths and block tables)",
+        "config": {
+            "workload": w.name,
+            "decode_seqs": int(len(w.dec_context_lens)) if has_dec else 0,
+            "prefill_seqs": int(len(w.cu_seqlens_q) - 1) if has_pre else 0,
+            "new_tokens": int(len(w.slot_mapping)),
+            "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+            "block_size": w.block_size, "num_blocks": w.num_blocks,
+            "value_definition": "decode algorithmic K/V bytes (logical, each sequence's context read once per KV "
+                                "head) per whole-step wall time" if has_dec else "prefill flops per step time",
+            "decode_kv_gb": round(kv_bytes / 1e9, 4),
+            "parallelism": "single-gpu",
+        },
+        "kernels": kernels,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,208 @@
+/*
+ * pkv.h -- C ABI of the paged-KV GQA attention library (libpkv.so, gfx950).
+ *
+ * Three operations of a block-paged inference engine's attention layer, as
+ * the nano-vLLM pages describe them: the KV-cache write through a slot
+ * mapping, decode attention over the paged cache, and causal varlen prefill
+ * attention ("Uses the flash-attn library for both prefill ... and decode
+ * ... A custom Triton kernel ... writes KV cache entries into the paged
+ * cache blocks", "Nano-vLLM Architecture and Performance", section
+ * "FlashAttention Integration"; "Attention stores the newly computed K/V into
+ * the KV Cache, then uses FlashAttention", "Project overview and the
+ * four-layer architecture", section "Lifecycle of one request", step 4).
+ *
+ * Conventions for every call
+ * --------------------------
+ * - Every pointer argument is a DEVICE pointer unless stated otherwise.  The
+ *   caller allocates, owns and frees every buffer; the library never
+ *   allocates device memory and keeps no state between calls.
+ * - Every call is asynchronous: it enqueues work on `stream` (a hipStream_t
+ *   passed as void*, NULL = the default stream) and returns without
+ *   synchronizing.  Calls are reentrant and thread-safe.
+ * - Element types: `dtype` is PKV_F32 (float) or PKV_BF16 (bfloat16 bit
+ *   patterns).  Outputs have the input dtype.  All metadata is int32; element
+ *   offsets are computed in 64 bits.
+ * - KV cache layout (a reading; the pages print none):
+ *       k_cache, v_cache: [num_blocks, block_size, num_kv_heads, head_dim],
+ *       row-major, head_dim contiguous, 16-byte aligned.
+ *   The token at absolute position p of sequence b lives in physical block
+ *   block_tables[b * max_blocks_per_seq + p / block_size], row p % block_size;
+ *   its slot is block * block_size + row.
+ * - GQA: query head h reads KV head h / (num_q_heads / num_kv_heads) (X-Ray
+ *   panel of the nano-vllm README: 32 query heads share 8 KV heads).
+ * - Supported shapes: head_dim 64 or 128; block_size a power of two in
+ *   [8, 1024]; num_q_heads / num_kv_heads in {1, 2, 4, 8}; 1 <= num_kv_heads <= 64.
+ *   Other shapes return PKV_ERR_UNSUPPORTED.
+ * - Errors: the return value is PKV_OK (0) or a negative pkv_status.  Argument
+ *   errors are detected on the host before anything is enqueued.  A failed
+ *   launch returns PKV_ERR_HIP.  pkv_last_error() gives a thread-local text
+ *   for the last non-OK return.  Device-side preconditions (block ids in
+ *   [0, num_blocks), distinct slots, 0 <= context_lens <= max_context_len,
+ *   cu_seqlens non-decreasing with Lq <= Lk) are the caller's to keep and are
+ *   not checked on the device; breaking them gives undefined results.
+ * - Zero sizes (num_tokens == 0, num_seqs == 0) return PKV_OK without a launch.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PKV_F32 = 0, PKV_BF16 = 1 } pkv_dtype;
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent sizes */
+  PKV_ERR_UNSUPPORTED = -2, /* valid but not built: head_dim, block size, group size, dtype */
+  PKV_ERR_WORKSPACE = -3,   /* decode workspace missing or too small */
+  PKV_ERR_HIP = -4          /* the HIP runtime reported an error (text in pkv_last_error) */
+} pkv_status;
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int pkv_version(void);
+
+/* Text of a status code (static storage). */
+const char* pkv_status_string(int status);
+
+/* Thread-local description of the last non-OK return on this thread. */
+const char* pkv_last_error(void);
+
+/*
+ * kv_store -- write the K and V rows of num_tokens new tokens into the paged
+ * caches ("store_kvcache_kernel ... writes KV cache entries into the paged
+ * cache blocks", "Nano-vLLM Architecture and Performance", section
+ * "FlashAttention Integration"; ModelRunner builds the slot_mapping, section
+ * "How It Works End-to-End").
+ *
+ *   k, v          [num_tokens, num_kv_heads, head_dim], contiguous, read only.
+ *   k_cache,
+ *   v_cache       [num_blocks, block_size, num_kv_heads, head_dim], written.
+ *   slot_mapping  [num_tokens] int32.  Token i goes to slot slot_mapping[i]
+ *                 (block = slot / block_size, row = slot % block_size).  A
+ *                 negative slot skips the token.  Non-negative slots must be
+ *                 distinct and < num_blocks * block_size.
+ *
+ * A pure copy of the stored bits: the caches change only at the named slots.
+ */
+int pkv_kv_store(const void* k, const void* v, void* k_cache, void* v_cache, const int32_t* slot_mapping,
+                 int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                 int32_t block_size, int32_t dtype, void* stream);
+
+/*
+ * Decode attention, split-K.  Sequence b's single query q[b] attends all
+ * context_lens[b] tokens of its context (the token just stored included),
+ * read through row b of block_tables: out = softmax(scale * q K^T) V per
+ * query head ("decode computes one token per sequence per step and is
+ * memory-bound", "Project overview and the four-layer architecture", section
+ * "Lifecycle of one request").
+ *
+ * The context is cut into splits of split_tokens tokens; each split's
+ * unnormalised softmax state (running max, sum, weighted V) goes to the
+ * workspace, and a reduction pass merges the splits of each (sequence, head).
+ * A sequence that fits one split has its output written by the first pass.
+ *
+ * pkv_decode_split_tokens returns the split length the library picks for a
+ * shape (a multiple of 64); pass it, or 0 for the same choice, or any
+ * positive multiple of 64.
+ * pkv_decode_workspace_bytes gives the workspace size that split length
+ * needs (0 when no sequence can span two splits).
+ */
+int32_t pkv_decode_split_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t max_context_len, int32_t block_size, int32_t dtype);
+
+int64_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                   int32_t max_context_len, int32_t split_tokens);
+
+/*
+ *   q               [num_seqs, num_q_heads, head_dim]
+ *   k_cache,v_cache [num_blocks, block_size, num_kv_heads, head_dim], read only
+ *   block_tables    [num_seqs, max_blocks_per_seq] int32 physical block ids
+ *   context_lens    [num_seqs] int32, 0 <= context_lens[b] <= max_context_len
+ *                   (0 gives an output row of zeros)
+ *   max_context_len host int, at most max_blocks_per_seq * block_size
+ *   scale           softmax scale (usually 1 / sqrt(head_dim))
+ *   out             [num_seqs, num_q_heads, head_dim], written; must not alias an input
+ *   split_tokens    0 or a positive multiple of 64
+ *   workspace       device scratch of at least
+ *                   pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+ *                   max_context_len, split) bytes (may be NULL when that is 0);
+ *                   its contents on entry do not matter.
+ */
+int pkv_paged_decode_attn(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
+                          float scale, void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int64_t num_blocks, int32_t block_size, int32_t dtype,
+                          int32_t split_tokens, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* The two passes of pkv_paged_decode_attn, enqueued separately (same
+ * arguments; call split then reduce on one stream).  Together they do
+ * exactly what pkv_paged_decode_attn does. */
+int pkv_paged_decode_split(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
+                           float scale, void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int64_t num_blocks, int32_t block_size, int32_t dtype,
+                           int32_t split_tokens, void* workspace, int64_t workspace_bytes, void* stream);
+
+int pkv_paged_decode_reduce(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
+                            float scale, void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int64_t num_blocks, int32_t block_size, int32_t dtype,
+                            int32_t split_tokens, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * Causal varlen prefill attention (chunked prefill and cached prefixes).
+ * Sequence b has Lq = cu_seqlens_q[b+1] - cu_seqlens_q[b] new queries and
+ * Lk = cu_seqlens_k[b+1] - cu_seqlens_k[b] keys in all, Lq <= Lk.  Query i
+ * sits at position Lk - Lq + i and attends keys 0 .. Lk - Lq + i (the causal
+ * rule "tokens can only see past tokens", nano-vllm README, tutorial chapter
+ * "Self-Attention"; aligned to the newest token so that a chunk after a
+ * cached prefix gives what full recomputation would, README section on the
+ * KV cache: only the new tokens are computed).
+ *
+ *   q             [total_q, num_q_heads, head_dim], rows cu_seqlens_q[b] + i
+ *   k, v          block_tables != NULL: the caches
+ *                 [num_blocks, block_size, num_kv_heads, head_dim] (the new
+ *                 tokens already stored by pkv_kv_store); block_tables == NULL:
+ *                 packed [num_blocks, num_kv_heads, head_dim] rows, sequence
+ *                 b's key t at row cu_seqlens_k[b] + t (num_blocks is then the
+ *                 row count and block_size is ignored).
+ *   cu_seqlens_q,
+ *   cu_seqlens_k  [num_seqs + 1] int32, starting at 0, non-decreasing.
+ *   block_tables  [num_seqs, max_blocks_per_seq] int32 or NULL.
+ *   out           [total_q, num_q_heads, head_dim], written; must not alias an input.
+ *   scale         softmax scale; scale <= 0 selects 1 / sqrt(head_dim).
+ *   max_seqlen_q,
+ *   max_seqlen_k  host bounds on Lq and Lk over the sequences.
+ *
+ * bf16 runs on the matrix cores (bf16 operands, fp32 accumulation, the
+ * softmax weights rounded to bf16 before they multiply V); fp32 runs on the
+ * vector units in fp32.
+ */
+int pkv_paged_prefill_attn(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                           const int32_t* cu_seqlens_k, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           void* out, float scale, int32_t num_seqs, int64_t total_q, int32_t max_seqlen_q,
+                           int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int64_t num_blocks, int32_t block_size, int32_t dtype, void* stream);
+
+/*
+ * Block gather (a check of the paged addressing every kernel uses): copy the
+ * Lk_b = cu_seqlens_k[b+1] - cu_seqlens_k[b] logical tokens of each sequence,
+ * read through its block table, to rows cu_seqlens_k[b] .. of k_out / v_out
+ * ([cu_seqlens_k[num_seqs], num_kv_heads, head_dim]).  Bit-exact copy
+ * ("PagedAttention: Allocate blocks on-demand" diagram of the nano-vllm
+ * README: a sequence's blocks need not be contiguous).
+ */
+int pkv_paged_gather(const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* cu_seqlens_k, int32_t num_seqs,
+                     int32_t max_seqlen_k, void* k_out, void* v_out, int32_t num_kv_heads, int32_t head_dim,
+                     int64_t num_blocks, int32_t block_size, int32_t dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

@@ -1,0 +1,265 @@
+"""Paged-KV GQA attention for AMD MI355X (gfx950): Python binding of libpkv.so.
+
+The binding only marshals arguments: it checks tensor shapes, dtypes and
+devices, derives the sizes, and calls the C ABI (include/pkv.h) with raw
+device pointers and the current HIP stream.  Every step of the computation
+runs in the library's HIP kernels.  There is no fallback: if libpkv.so has not
+been built (``python -m paged_kv_gqa_mapping_amd.build``) every call raises.
+
+Entry points (names follow the operations of a nano-vLLM style engine):
+
+* ``kv_store(k, v, k_cache, v_cache, slot_mapping)``
+* ``paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, scale, out)``
+* ``paged_prefill_attn(q, k, v, cu_seqlens_q, cu_seqlens_k, block_tables, out)``
+* ``paged_gather(k_cache, v_cache, block_tables, cu_seqlens_k)``
+
+Tensors: caches ``[num_blocks, block_size, num_kv_heads, head_dim]``;
+``torch.bfloat16`` or ``torch.float32``; metadata ``torch.int32``; all on the
+GPU and contiguous.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "kv_store",
+    "paged_decode_attn",
+    "paged_decode_split",
+    "paged_decode_reduce",
+    "paged_prefill_attn",
+    "paged_gather",
+    "decode_split_tokens",
+    "decode_workspace_bytes",
+    "lib",
+    "library_path",
+    "PkvError",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libpkv.so")
+
+PKV_F32 = 0
+PKV_BF16 = 1
+
+_lib = None
+
+
+class PkvError(RuntimeError):
+    """A non-OK status from libpkv.so (message from pkv_last_error)."""
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libpkv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise PkvError(f"{library_path} is missing: build it with `python -m paged_kv_gqa_mapping_amd.build`")
+    L = ctypes.CDLL(library_path)
+    P, I32, I64, F, V = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+    L.pkv_version.restype = ctypes.c_int
+    L.pkv_status_string.restype = ctypes.c_char_p
+    L.pkv_status_string.argtypes = [ctypes.c_int]
+    L.pkv_last_error.restype = ctypes.c_char_p
+    L.pkv_kv_store.argtypes = [P, P, P, P, P, I64, I32, I32, I64, I32, I32, V]
+    L.pkv_kv_store.restype = ctypes.c_int
+    L.pkv_decode_split_tokens.argtypes = [I32, I32, I32, I32, I32, I32, I32]
+    L.pkv_decode_split_tokens.restype = I32
+    L.pkv_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
+    L.pkv_decode_workspace_bytes.restype = I64
+    dec = [P, P, P, P, I32, P, I32, F, P, I32, I32, I32, I32, I64, I32, I32, I32, P, I64, V]
+    for name in ("pkv_paged_decode_attn", "pkv_paged_decode_split", "pkv_paged_decode_reduce"):
+        getattr(L, name).argtypes = dec
+        getattr(L, name).restype = ctypes.c_int
+    L.pkv_paged_prefill_attn.argtypes = [P, P, P, P, P, P, I32, P, F, I32, I64, I32, I32, I32, I32, I32, I64, I32,
+                                         I32, V]
+    L.pkv_paged_prefill_attn.restype = ctypes.c_int
+    L.pkv_paged_gather.argtypes = [P, P, P, I32, P, I32, I32, P, P, I32, I32, I64, I32, I32, V]
+    L.pkv_paged_gather.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        L = lib()
+        raise PkvError(f"{L.pkv_status_string(status).decode()}: {L.pkv_last_error().decode()}")
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    if t.dtype == torch.float32:
+        return PKV_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+
+
+def _dev(t, name, dtype=None, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    return t
+
+
+def _stream() -> int:
+    return _torch().cuda.current_stream().cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def kv_store(k, v, k_cache, v_cache, slot_mapping) -> None:
+    """Write token i's K/V rows ([N, Hkv, D]) to cache slot slot_mapping[i] (negative: skip)."""
+    torch = _torch()
+    _dev(k, "k", ndim=3)
+    _dev(v, "v", k.dtype, 3)
+    _dev(k_cache, "k_cache", k.dtype, 4)
+    _dev(v_cache, "v_cache", k.dtype, 4)
+    _dev(slot_mapping, "slot_mapping", torch.int32, 1)
+    N, Hkv, D = k.shape
+    NB, bs, Hkv2, D2 = k_cache.shape
+    if v.shape != k.shape or v_cache.shape != k_cache.shape or (Hkv2, D2) != (Hkv, D) or slot_mapping.shape[0] != N:
+        raise ValueError("shape mismatch among k, v, k_cache, v_cache, slot_mapping")
+    _check(lib().pkv_kv_store(_ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), N, Hkv, D, NB, bs,
+                              _dtype_code(k), _stream()))
+
+
+def decode_split_tokens(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, block_size, dtype_code):
+    return int(lib().pkv_decode_split_tokens(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                                             block_size, dtype_code))
+
+
+def decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, split_tokens) -> int:
+    return int(lib().pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, split_tokens))
+
+
+def _decode(fn_name, q, k_cache, v_cache, block_tables, context_lens, scale, out, max_context_len, split_tokens,
+            workspace):
+    torch = _torch()
+    _dev(q, "q", ndim=3)
+    _dev(k_cache, "k_cache", q.dtype, 4)
+    _dev(v_cache, "v_cache", q.dtype, 4)
+    _dev(block_tables, "block_tables", torch.int32, 2)
+    _dev(context_lens, "context_lens", torch.int32, 1)
+    _dev(out, "out", q.dtype, 3)
+    B, Hq, D = q.shape
+    NB, bs, Hkv, D2 = k_cache.shape
+    if v_cache.shape != k_cache.shape or D2 != D or out.shape != q.shape:
+        raise ValueError("shape mismatch among q, k_cache, v_cache, out")
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables and context_lens need one row per sequence")
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if B else 0
+    code = _dtype_code(q)
+    split = int(split_tokens) or decode_split_tokens(B, Hq, Hkv, D, max_context_len, bs, code)
+    need = decode_workspace_bytes(B, Hq, D, max_context_len, split)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(getattr(lib(), fn_name)(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        int(max_context_len), float(scale), _ptr(out), B, Hq, Hkv, D, NB, bs, code, split, _ptr(workspace), ws_bytes,
+        _stream()))
+    return out
+
+
+def paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, scale, out, max_context_len=None,
+                      split_tokens=0, workspace=None):
+    """Decode attention: q [B, Hq, D] over each sequence's context_lens[b] cached tokens -> out [B, Hq, D]."""
+    return _decode("pkv_paged_decode_attn", q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                   max_context_len, split_tokens, workspace)
+
+
+def paged_decode_split(q, k_cache, v_cache, block_tables, context_lens, scale, out, max_context_len=None,
+                       split_tokens=0, workspace=None):
+    """First pass of paged_decode_attn (per-split softmax states)."""
+    return _decode("pkv_paged_decode_split", q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                   max_context_len, split_tokens, workspace)
+
+
+def paged_decode_reduce(q, k_cache, v_cache, block_tables, context_lens, scale, out, max_context_len=None,
+                        split_tokens=0, workspace=None):
+    """Second pass of paged_decode_attn (merge of the split states); same arguments and workspace as the first."""
+    return _decode("pkv_paged_decode_reduce", q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                   max_context_len, split_tokens, workspace)
+
+
+def paged_prefill_attn(q, k, v, cu_seqlens_q, cu_seqlens_k, block_tables, out, max_seqlen_q=None,
+                       max_seqlen_k=None, scale=None):
+    """Causal varlen prefill: q [sum Lq, Hq, D]; k, v the caches (block_tables given) or packed [sum Lk, Hkv, D]."""
+    torch = _torch()
+    _dev(q, "q", ndim=3)
+    _dev(out, "out", q.dtype, 3)
+    _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+    _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+    Tq, Hq, D = q.shape
+    B = cu_seqlens_q.shape[0] - 1
+    if cu_seqlens_k.shape[0] != B + 1 or out.shape != q.shape:
+        raise ValueError("cu_seqlens_q / cu_seqlens_k / out shape mismatch")
+    if block_tables is not None:
+        _dev(k, "k", q.dtype, 4)
+        _dev(v, "v", q.dtype, 4)
+        _dev(block_tables, "block_tables", torch.int32, 2)
+        NB, bs, Hkv, D2 = k.shape
+        W = block_tables.shape[1]
+        if block_tables.shape[0] != B:
+            raise ValueError("block_tables needs one row per sequence")
+    else:
+        _dev(k, "k", q.dtype, 3)
+        _dev(v, "v", q.dtype, 3)
+        NB, Hkv, D2 = k.shape
+        bs, W = 0, 0
+    if v.shape != k.shape or D2 != D:
+        raise ValueError("shape mismatch among q, k, v")
+    if max_seqlen_q is None or max_seqlen_k is None:
+        cq = cu_seqlens_q.cpu()
+        ck = cu_seqlens_k.cpu()
+        max_seqlen_q = int((cq[1:] - cq[:-1]).max()) if B else 0
+        max_seqlen_k = int((ck[1:] - ck[:-1]).max()) if B else 0
+    sc = 0.0 if scale is None else float(scale)
+    _check(lib().pkv_paged_prefill_attn(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(block_tables), W, _ptr(out), sc, B,
+        Tq, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D, NB, bs, _dtype_code(q), _stream()))
+    return out
+
+
+def paged_gather(k_cache, v_cache, block_tables, cu_seqlens_k, max_seqlen_k=None, k_out=None, v_out=None):
+    """Copy each sequence's logical K/V rows, read through its block table, to packed [sum Lk, Hkv, D] buffers."""
+    torch = _torch()
+    _dev(k_cache, "k_cache", ndim=4)
+    _dev(v_cache, "v_cache", k_cache.dtype, 4)
+    _dev(block_tables, "block_tables", torch.int32, 2)
+    _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+    NB, bs, Hkv, D = k_cache.shape
+    B = cu_seqlens_k.shape[0] - 1
+    ck = cu_seqlens_k.cpu()
+    total = int(ck[-1]) if B >= 0 else 0
+    if max_seqlen_k is None:
+        max_seqlen_k = int((ck[1:] - ck[:-1]).max()) if B else 0
+    if k_out is None:
+        k_out = torch.empty((total, Hkv, D), dtype=k_cache.dtype, device=k_cache.device)
+    if v_out is None:
+        v_out = torch.empty((total, Hkv, D), dtype=k_cache.dtype, device=k_cache.device)
+    _dev(k_out, "k_out", k_cache.dtype, 3)
+    _dev(v_out, "v_out", k_cache.dtype, 3)
+    _check(lib().pkv_paged_gather(
+        _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1], _ptr(cu_seqlens_k), B,
+        int(max_seqlen_k), _ptr(k_out), _ptr(v_out), Hkv, D, NB, bs, _dtype_code(k_cache), _stream()))
+    return k_out, v_out

@@ -1,0 +1,332 @@
+// C ABI of libpkv.so: argument checks, split choice, and launches on the
+// caller's stream.  Declarations and the full contract are in include/pkv.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/pkv.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PKV_OK;
+  return fail(PKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elt_bytes(int32_t dtype) { return dtype == PKV_BF16 ? 2 : 4; }
+
+int log2_exact(int32_t x) {
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return (1 << l) == x ? l : -1;
+}
+
+// Shape checks common to every call on the cache.
+int check_cache_shape(int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, int32_t block_size, int32_t dtype,
+                      bool paged) {
+  if (dtype != PKV_F32 && dtype != PKV_BF16) return fail(PKV_ERR_UNSUPPORTED, "dtype %d is not PKV_F32 or PKV_BF16", dtype);
+  if (num_kv_heads < 1 || num_kv_heads > 64)
+    return fail(num_kv_heads < 1 ? PKV_ERR_INVALID_ARG : PKV_ERR_UNSUPPORTED, "num_kv_heads %d outside [1, 64]",
+                num_kv_heads);
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_ERR_UNSUPPORTED, "head_dim %d is not 64 or 128", head_dim);
+  if (num_blocks < 1) return fail(PKV_ERR_INVALID_ARG, "num_blocks %lld < 1", (long long)num_blocks);
+  if (paged) {
+    const int lb = log2_exact(block_size);
+    if (block_size < 8 || block_size > 1024 || lb < 0)
+      return fail(PKV_ERR_UNSUPPORTED, "block_size %d is not a power of two in [8, 1024]", block_size);
+  }
+  return PKV_OK;
+}
+
+int check_heads(int32_t num_q_heads, int32_t num_kv_heads) {
+  if (num_q_heads < 1 || num_q_heads % num_kv_heads)
+    return fail(PKV_ERR_INVALID_ARG, "num_q_heads %d is not a positive multiple of num_kv_heads %d", num_q_heads,
+                num_kv_heads);
+  const int G = num_q_heads / num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8)
+    return fail(PKV_ERR_UNSUPPORTED, "group size %d (num_q_heads / num_kv_heads) is not 1, 2, 4 or 8", G);
+  return PKV_OK;
+}
+
+int32_t round_up(int64_t x, int32_t m) { return (int32_t)(((x + m - 1) / m) * m); }
+
+// Split length for decode (tokens, multiple of 64): aim for ~4096 waves over
+// the grid so that every CU has work to hide latency with, but keep splits at
+// least 256 tokens long so the partial states stay small next to the KV bytes.
+int32_t auto_split(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
+  if (max_context_len <= 256) return round_up(std::max(max_context_len, 1), 64);
+  const int64_t base = (int64_t)num_seqs * std::max(1, num_kv_heads / 8);
+  const int64_t want_splits = std::max<int64_t>(1, (4096 + base - 1) / base);
+  int32_t split = round_up((max_context_len + want_splits - 1) / want_splits, 64);
+  split = std::max(split, 256);
+  return std::min(split, round_up(max_context_len, 64));
+}
+
+struct DecodeCall {
+  pkv::RowAttnArgs args;
+  int32_t dtype;
+  int32_t head_dim;
+  bool empty;
+};
+
+int prepare_decode(DecodeCall& call, const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                   int32_t max_context_len, float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                   int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, int32_t block_size, int32_t dtype,
+                   int32_t split_tokens, void* workspace, int64_t workspace_bytes) {
+  call.empty = false;
+  if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
+  int st = check_cache_shape(num_kv_heads, head_dim, num_blocks, block_size, dtype, true);
+  if (st) return st;
+  st = check_heads(num_q_heads, num_kv_heads);
+  if (st) return st;
+  if (num_seqs == 0) {
+    call.empty = true;
+    return PKV_OK;
+  }
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || !out)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer among q, k_cache, v_cache, block_tables, context_lens, out");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return fail(PKV_ERR_INVALID_ARG, "q, k_cache, v_cache and out must be 16-byte aligned");
+  if (max_blocks_per_seq < 1) return fail(PKV_ERR_INVALID_ARG, "max_blocks_per_seq %d < 1", max_blocks_per_seq);
+  if (max_context_len < 0 || (int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PKV_ERR_INVALID_ARG, "max_context_len %d outside [0, max_blocks_per_seq * block_size = %lld]",
+                max_context_len, (long long)max_blocks_per_seq * block_size);
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
+  if (split_tokens < 0 || split_tokens % 64)
+    return fail(PKV_ERR_INVALID_ARG, "split_tokens %d is not 0 or a positive multiple of 64", split_tokens);
+  const int32_t split = split_tokens ? split_tokens : auto_split(num_seqs, num_kv_heads, max_context_len);
+  const int32_t S = std::max(1, (max_context_len + split - 1) / split);
+  const int64_t need = pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, split);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PKV_ERR_WORKSPACE, "decode workspace of %lld bytes needed, %lld given%s", (long long)need,
+                (long long)workspace_bytes, workspace ? "" : " (NULL)");
+  if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 15u))
+    return fail(PKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if ((int64_t)num_seqs * (num_kv_heads) * S > 0x7fffffffLL)
+    return fail(PKV_ERR_UNSUPPORTED, "grid too large: reduce num_seqs or raise split_tokens");
+
+  pkv::RowAttnArgs& a = call.args;
+  a = pkv::RowAttnArgs{};
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = out;
+  a.ws_o = need > 0 ? static_cast<float*>(workspace) : nullptr;
+  a.ws_ml = need > 0 ? a.ws_o + (int64_t)num_seqs * num_q_heads * S * head_dim : nullptr;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.log2_block_size = log2_exact(block_size);
+  a.split_tokens = split;
+  a.num_splits = S;
+  call.dtype = dtype;
+  call.head_dim = head_dim;
+  if (!pkv::row_attn_supported(dtype, head_dim, num_q_heads, num_kv_heads))
+    return fail(PKV_ERR_UNSUPPORTED, "no decode kernel for dtype %d, head_dim %d, %d/%d heads", dtype, head_dim,
+                num_q_heads, num_kv_heads);
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_version(void) { return 100; }
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "PKV_OK";
+    case PKV_ERR_INVALID_ARG: return "PKV_ERR_INVALID_ARG";
+    case PKV_ERR_UNSUPPORTED: return "PKV_ERR_UNSUPPORTED";
+    case PKV_ERR_WORKSPACE: return "PKV_ERR_WORKSPACE";
+    case PKV_ERR_HIP: return "PKV_ERR_HIP";
+  }
+  return "unknown pkv status";
+}
+
+const char* pkv_last_error(void) { return g_last_error.c_str(); }
+
+int pkv_kv_store(const void* k, const void* v, void* k_cache, void* v_cache, const int32_t* slot_mapping,
+                 int64_t num_tokens, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, int32_t block_size,
+                 int32_t dtype, void* stream) {
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_tokens %lld < 0", (long long)num_tokens);
+  int st = check_cache_shape(num_kv_heads, head_dim, num_blocks, block_size, dtype, true);
+  if (st) return st;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer among k, v, k_cache, v_cache, slot_mapping");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_ERR_INVALID_ARG, "k, v, k_cache and v_cache must be 16-byte aligned");
+  if (num_tokens > 0x7fffffffLL * 4) return fail(PKV_ERR_UNSUPPORTED, "num_tokens %lld too large", (long long)num_tokens);
+  const int32_t row_bytes = num_kv_heads * head_dim * elt_bytes(dtype);
+  return hip_status(pkv::launch_kv_store(k, v, k_cache, v_cache, slot_mapping, num_tokens, row_bytes,
+                                         static_cast<hipStream_t>(stream)),
+                    "kv_store launch");
+}
+
+int32_t pkv_decode_split_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                int32_t max_context_len, int32_t block_size, int32_t dtype) {
+  (void)num_q_heads;
+  (void)head_dim;
+  (void)block_size;
+  (void)dtype;
+  return auto_split(std::max(num_seqs, 1), std::max(num_kv_heads, 1), std::max(max_context_len, 0));
+}
+
+int64_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
+                                   int32_t split_tokens) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0 || split_tokens <= 0) return 0;
+  const int64_t S = (max_context_len + (int64_t)split_tokens - 1) / split_tokens;
+  if (S <= 1) return 0;
+  return (int64_t)num_seqs * num_q_heads * S * (head_dim + 2) * (int64_t)sizeof(float);
+}
+
+#define PKV_DECODE_ARGS                                                                                        \
+  const void *q, const void *k_cache, const void *v_cache, const int32_t *block_tables,                      \
+      int32_t max_blocks_per_seq, const int32_t *context_lens, int32_t max_context_len, float scale, void *out, \
+      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,      \
+      int32_t block_size, int32_t dtype, int32_t split_tokens, void *workspace, int64_t workspace_bytes,      \
+      void *stream
+#define PKV_DECODE_FWD                                                                                        \
+  q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, max_context_len, scale, out, num_seqs, \
+      num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, dtype, split_tokens, workspace, workspace_bytes
+
+int pkv_paged_decode_split(PKV_DECODE_ARGS) {
+  DecodeCall call;
+  int st = prepare_decode(call, PKV_DECODE_FWD);
+  if (st || call.empty) return st;
+  return hip_status(pkv::launch_row_attn(call.args, call.dtype, call.head_dim, false, static_cast<hipStream_t>(stream)),
+                    "decode split launch");
+}
+
+int pkv_paged_decode_reduce(PKV_DECODE_ARGS) {
+  DecodeCall call;
+  int st = prepare_decode(call, PKV_DECODE_FWD);
+  if (st || call.empty) return st;
+  if (call.args.num_splits <= 1) return PKV_OK;
+  return hip_status(pkv::launch_decode_reduce(call.args, call.dtype, call.head_dim, static_cast<hipStream_t>(stream)),
+                    "decode reduce launch");
+}
+
+int pkv_paged_decode_attn(PKV_DECODE_ARGS) {
+  DecodeCall call;
+  int st = prepare_decode(call, PKV_DECODE_FWD);
+  if (st || call.empty) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(pkv::launch_row_attn(call.args, call.dtype, call.head_dim, false, s), "decode split launch");
+  if (st || call.args.num_splits <= 1) return st;
+  return hip_status(pkv::launch_decode_reduce(call.args, call.dtype, call.head_dim, s), "decode reduce launch");
+}
+
+int pkv_paged_prefill_attn(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                           const int32_t* cu_seqlens_k, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           void* out, float scale, int32_t num_seqs, int64_t total_q, int32_t max_seqlen_q,
+                           int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int64_t num_blocks, int32_t block_size, int32_t dtype, void* stream) {
+  if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return fail(PKV_ERR_INVALID_ARG, "negative size");
+  const bool paged = block_tables != nullptr;
+  int st = check_cache_shape(num_kv_heads, head_dim, num_blocks, block_size, dtype, paged);
+  if (st) return st;
+  st = check_heads(num_q_heads, num_kv_heads);
+  if (st) return st;
+  if (num_seqs == 0 || total_q == 0 || max_seqlen_q == 0) return PKV_OK;
+  if (!q || !k || !v || !cu_seqlens_q || !cu_seqlens_k || !out)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer among q, k, v, cu_seqlens_q, cu_seqlens_k, out");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(PKV_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+  if (max_seqlen_q > max_seqlen_k)
+    return fail(PKV_ERR_INVALID_ARG, "max_seqlen_q %d > max_seqlen_k %d", max_seqlen_q, max_seqlen_k);
+  if (paged && (max_blocks_per_seq < 1 || (int64_t)max_seqlen_k > (int64_t)max_blocks_per_seq * block_size))
+    return fail(PKV_ERR_INVALID_ARG, "max_seqlen_k %d exceeds max_blocks_per_seq %d * block_size %d", max_seqlen_k,
+                max_blocks_per_seq, block_size);
+  if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)head_dim);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == PKV_BF16) {
+    pkv::PrefillArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.block_tables = block_tables;
+    a.cu_seqlens_q = cu_seqlens_q;
+    a.cu_seqlens_k = cu_seqlens_k;
+    a.out = out;
+    a.scale_log2 = sc * 1.4426950408889634f;
+    a.num_seqs = num_seqs;
+    a.num_q_heads = num_q_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.max_blocks_per_seq = max_blocks_per_seq;
+    a.log2_block_size = paged ? log2_exact(block_size) : 0;
+    a.max_seqlen_q = max_seqlen_q;
+    return hip_status(pkv::launch_prefill_mfma(a, head_dim, s), "prefill launch");
+  }
+  if (!pkv::row_attn_supported(dtype, head_dim, num_q_heads, num_kv_heads))
+    return fail(PKV_ERR_UNSUPPORTED, "no prefill kernel for dtype %d, head_dim %d, %d/%d heads", dtype, head_dim,
+                num_q_heads, num_kv_heads);
+  pkv::RowAttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.block_tables = block_tables;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.cu_seqlens_k = cu_seqlens_k;
+  a.out = out;
+  a.scale_log2 = sc * 1.4426950408889634f;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.log2_block_size = paged ? log2_exact(block_size) : 0;
+  a.max_rows = max_seqlen_q;
+  return hip_status(pkv::launch_row_attn(a, dtype, head_dim, true, s), "prefill launch");
+}
+
+int pkv_paged_gather(const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_k,
+                     void* k_out, void* v_out, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,
+                     int32_t block_size, int32_t dtype, void* stream) {
+  if (num_seqs < 0 || max_seqlen_k < 0) return fail(PKV_ERR_INVALID_ARG, "negative size");
+  int st = check_cache_shape(num_kv_heads, head_dim, num_blocks, block_size, dtype, true);
+  if (st) return st;
+  if (num_seqs == 0 || max_seqlen_k == 0) return PKV_OK;
+  if (num_seqs > 65535) return fail(PKV_ERR_UNSUPPORTED, "gather handles at most 65535 sequences per call");
+  if (!k_cache || !v_cache || !block_tables || !cu_seqlens_k || !k_out || !v_out)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_out) || !aligned16(v_out))
+    return fail(PKV_ERR_INVALID_ARG, "caches and outputs must be 16-byte aligned");
+  if (max_blocks_per_seq < 1 || (int64_t)max_seqlen_k > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PKV_ERR_INVALID_ARG, "max_seqlen_k %d exceeds max_blocks_per_seq %d * block_size %d", max_seqlen_k,
+                max_blocks_per_seq, block_size);
+  const int32_t row_bytes = num_kv_heads * head_dim * elt_bytes(dtype);
+  return hip_status(pkv::launch_gather(k_cache, v_cache, block_tables, max_blocks_per_seq, cu_seqlens_k, num_seqs,
+                                       max_seqlen_k, k_out, v_out, row_bytes, log2_exact(block_size),
+                                       static_cast<hipStream_t>(stream)),
+                    "gather launch");
+}
+
+}  // extern "C"

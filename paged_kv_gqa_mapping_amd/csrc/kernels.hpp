@@ -1,0 +1,71 @@
+// Host-side launchers of the device kernels (one per translation unit).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+enum Dtype : int32_t { kF32 = 0, kBF16 = 1 };
+
+hipError_t launch_kv_store(const void* k, const void* v, void* k_cache, void* v_cache, const int32_t* slot_mapping,
+                           int64_t num_tokens, int32_t row_bytes, hipStream_t stream);
+
+hipError_t launch_gather(const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                         int32_t max_blocks_per_seq, const int32_t* cu_seqlens_k, int32_t num_seqs,
+                         int32_t max_seqlen_k, void* k_out, void* v_out, int32_t row_bytes, int32_t log2_block_size,
+                         hipStream_t stream);
+
+// Arguments of the row-attention kernel (decode rows, or prefill rows on the vector path).
+struct RowAttnArgs {
+  const void* q;            // decode: [B, Hq, D]; prefill: [total_q, Hq, D]
+  const void* k;            // paged caches or packed rows
+  const void* v;
+  const int32_t* block_tables;  // NULL: packed k/v rows (prefill only)
+  const int32_t* context_lens;  // decode: [B]
+  const int32_t* cu_seqlens_q;  // prefill: [B + 1]
+  const int32_t* cu_seqlens_k;  // prefill: [B + 1]
+  void* out;
+  float* ws_o;   // [B, Hq, S, D] fp32 partial outputs (decode, S > 1)
+  float* ws_ml;  // [B, Hq, S, 2] fp32 (running max in log2 units, sum)
+  float scale_log2;  // scale * log2(e)
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t max_blocks_per_seq;
+  int32_t log2_block_size;
+  int32_t split_tokens;  // decode: tokens per split
+  int32_t num_splits;    // decode: S, the split count of the grid (ceil(max_context_len / split_tokens))
+  int32_t max_rows;      // prefill: max_seqlen_q
+};
+
+// Picks the instantiation (dtype, head_dim, KV heads per wave, group size) and launches.
+// `prefill` selects prefill rows (causal, one split) instead of decode rows.
+hipError_t launch_row_attn(const RowAttnArgs& a, int32_t dtype, int32_t head_dim, bool prefill, hipStream_t stream);
+
+hipError_t launch_decode_reduce(const RowAttnArgs& a, int32_t dtype, int32_t head_dim, hipStream_t stream);
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* block_tables;
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  void* out;
+  float scale_log2;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t max_blocks_per_seq;
+  int32_t log2_block_size;
+  int32_t max_seqlen_q;
+};
+
+// bf16 matrix-core prefill.
+hipError_t launch_prefill_mfma(const PrefillArgs& a, int32_t head_dim, hipStream_t stream);
+
+// Row-attention instantiation exists for this shape?
+bool row_attn_supported(int32_t dtype, int32_t head_dim, int32_t num_q_heads, int32_t num_kv_heads);
+
+}  // namespace pkv

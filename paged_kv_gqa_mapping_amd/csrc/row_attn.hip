@@ -1,0 +1,105 @@
+// Instantiations and dispatch of the row-attention kernels (decode split,
+// decode reduce, fp32 prefill rows).
+#include "row_attn.hpp"
+
+namespace pkv {
+
+namespace {
+
+// KV heads per wave: the most of {8, 4, 2, 1} that divides num_kv_heads while
+// each lane still owns at least one 32-bit word of a row and holds at most 64
+// fp32 output accumulators (G heads x D / (64 / hpw) elements); if no choice
+// meets the second bound, the smallest that meets the first.
+int choose_hpw(int32_t dtype, int32_t head_dim, int32_t num_q_heads, int32_t num_kv_heads) {
+  const int elt = dtype == kBF16 ? 2 : 4;
+  const int G = num_q_heads / num_kv_heads;
+  int fallback = 0;
+  for (int hpw : {8, 4, 2, 1}) {
+    if (num_kv_heads % hpw) continue;
+    const int dpl = head_dim / (64 / hpw);
+    if (dpl * elt < 4) continue;
+    fallback = hpw;
+    if (G * dpl <= 64) return hpw;
+  }
+  return fallback;
+}
+
+template <bool BF16, int D, int HPW, int G, bool PREFILL>
+hipError_t launch_one(const RowAttnArgs& a, hipStream_t stream) {
+  constexpr int U = (BF16 && G <= 2) ? 4 : 2;  // tokens per step
+  const int n_hg = a.num_kv_heads / HPW;
+  const int64_t rows = PREFILL ? (int64_t)a.max_rows : (int64_t)a.num_splits;
+  const int64_t blocks = (int64_t)n_hg * a.num_seqs * rows;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((row_attn_kernel<BF16, D, HPW, G, U, PREFILL>), dim3((unsigned)blocks), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <bool BF16, int D, int HPW, bool PREFILL>
+hipError_t by_group(const RowAttnArgs& a, int G, hipStream_t stream) {
+  switch (G) {
+    case 1: return launch_one<BF16, D, HPW, 1, PREFILL>(a, stream);
+    case 2: return launch_one<BF16, D, HPW, 2, PREFILL>(a, stream);
+    case 4: return launch_one<BF16, D, HPW, 4, PREFILL>(a, stream);
+    case 8: return launch_one<BF16, D, HPW, 8, PREFILL>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <bool BF16, int D, bool PREFILL>
+hipError_t by_hpw(const RowAttnArgs& a, int hpw, int G, hipStream_t stream) {
+  switch (hpw) {
+    case 8: return by_group<BF16, D, 8, PREFILL>(a, G, stream);
+    case 4: return by_group<BF16, D, 4, PREFILL>(a, G, stream);
+    case 2: return by_group<BF16, D, 2, PREFILL>(a, G, stream);
+    case 1:
+      if constexpr (D * (BF16 ? 2 : 4) / 64 >= 4) return by_group<BF16, D, 1, PREFILL>(a, G, stream);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template <bool PREFILL>
+hipError_t dispatch(const RowAttnArgs& a, int32_t dtype, int32_t head_dim, hipStream_t stream) {
+  const int hpw = choose_hpw(dtype, head_dim, a.num_q_heads, a.num_kv_heads);
+  const int G = a.num_q_heads / a.num_kv_heads;
+  if (dtype == kBF16) {
+    if (head_dim == 128) return by_hpw<true, 128, PREFILL>(a, hpw, G, stream);
+    if (head_dim == 64) return by_hpw<true, 64, PREFILL>(a, hpw, G, stream);
+  } else {
+    if (head_dim == 128) return by_hpw<false, 128, PREFILL>(a, hpw, G, stream);
+    if (head_dim == 64) return by_hpw<false, 64, PREFILL>(a, hpw, G, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool row_attn_supported(int32_t dtype, int32_t head_dim, int32_t num_q_heads, int32_t num_kv_heads) {
+  if (dtype != kBF16 && dtype != kF32) return false;
+  if (head_dim != 64 && head_dim != 128) return false;
+  if (num_kv_heads < 1 || num_q_heads % num_kv_heads) return false;
+  const int G = num_q_heads / num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return false;
+  return choose_hpw(dtype, head_dim, num_q_heads, num_kv_heads) != 0;
+}
+
+hipError_t launch_row_attn(const RowAttnArgs& a, int32_t dtype, int32_t head_dim, bool prefill, hipStream_t stream) {
+  return prefill ? dispatch<true>(a, dtype, head_dim, stream) : dispatch<false>(a, dtype, head_dim, stream);
+}
+
+hipError_t launch_decode_reduce(const RowAttnArgs& a, int32_t dtype, int32_t head_dim, hipStream_t stream) {
+  const int64_t pairs = (int64_t)a.num_seqs * a.num_q_heads;
+  const int64_t blocks = (pairs + 3) / 4;
+  if (blocks <= 0) return hipSuccess;
+  dim3 grid((unsigned)blocks), block(256);
+  if (dtype == kBF16 && head_dim == 128) hipLaunchKernelGGL((decode_reduce_kernel<true, 128>), grid, block, 0, stream, a);
+  else if (dtype == kBF16 && head_dim == 64) hipLaunchKernelGGL((decode_reduce_kernel<true, 64>), grid, block, 0, stream, a);
+  else if (dtype == kF32 && head_dim == 128) hipLaunchKernelGGL((decode_reduce_kernel<false, 128>), grid, block, 0, stream, a);
+  else if (dtype == kF32 && head_dim == 64) hipLaunchKernelGGL((decode_reduce_kernel<false, 64>), grid, block, 0, stream, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace pkv

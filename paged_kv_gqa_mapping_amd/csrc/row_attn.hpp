@@ -1,0 +1,320 @@
+// Row attention on the vector units: one wave = one query row of every head
+// of HPW KV heads, streaming that row's keys through the block table.
+//
+//  * Decode: a row is sequence b's new token; its context is cut into splits
+//    of split_tokens keys, one wave per (sequence, KV-head group, split).
+//    Splits write an unnormalised softmax state that decode_reduce merges.
+//  * Prefill rows (fp32 path): query i of sequence b attends keys 0..p with
+//    p = Lk - Lq + i, in one split.
+//
+// Lane layout: the 64 lanes are HPW groups of TL = 64 / HPW lanes, one group
+// per KV head.  Lane c of a group owns DPL = D / TL elements of the head
+// dimension, as NCH chunks of CH bytes: chunk jj covers elements
+// [(jj * TL + c) * EPC, +EPC).  A load instruction then reads, for every head
+// of the group, TL * CH contiguous bytes of the token's row.  Each K/V byte is
+// loaded once and used for all G query heads that share the KV head (their
+// queries sit in the same lanes).
+//
+// Per step of U tokens: partial dot products per lane (bf16: v_dot2 on packed
+// pairs), an all-reduce over the TL lanes of the group with DPP, the online
+// softmax update (max in log2 units; the running reference max is only raised
+// when a score exceeds it by more than kTau, which keeps the weights <= 2^kTau
+// and skips most rescales), then weights times V accumulated in fp32.
+#pragma once
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace pkv {
+
+template <int CH>
+struct Chunk;
+template <>
+struct Chunk<16> {
+  typedef uint4 type;
+};
+template <>
+struct Chunk<8> {
+  typedef uint2 type;
+};
+template <>
+struct Chunk<4> {
+  typedef uint32_t type;
+};
+
+template <int CH>
+__device__ __forceinline__ void load_words(uint32_t* w, const char* p) {
+  typedef typename Chunk<CH>::type T;
+  T x = *reinterpret_cast<const T*>(p);
+  if constexpr (CH == 16) {
+    w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+  } else if constexpr (CH == 8) {
+    w[0] = x.x; w[1] = x.y;
+  } else {
+    w[0] = x;
+  }
+}
+
+template <int CH>
+__device__ __forceinline__ void store_words(char* p, const uint32_t* w) {
+  typedef typename Chunk<CH>::type T;
+  T x;
+  if constexpr (CH == 16) {
+    x.x = w[0]; x.y = w[1]; x.z = w[2]; x.w = w[3];
+  } else if constexpr (CH == 8) {
+    x.x = w[0]; x.y = w[1];
+  } else {
+    x = w[0];
+  }
+  *reinterpret_cast<T*>(p) = x;
+}
+
+template <bool BF16, int D, int HPW, int G, int U, bool PREFILL>
+__global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
+  constexpr int ELT = BF16 ? 2 : 4;
+  constexpr int TL = 64 / HPW;
+  constexpr int DPL = D / TL;
+  constexpr int LANE_BYTES = DPL * ELT;
+  static_assert(LANE_BYTES >= 4, "a lane must own at least one 32-bit word");
+  constexpr int CH = LANE_BYTES >= 16 ? 16 : LANE_BYTES;
+  constexpr int NCH = LANE_BYTES / CH;
+  constexpr int WPC = CH / 4;     // words per chunk
+  constexpr int NW = NCH * WPC;   // words per lane per row
+  constexpr int EPW = 4 / ELT;    // elements per word
+  constexpr int EPC = CH / ELT;   // elements per chunk
+
+  const int lane = threadIdx.x;
+  const int hl = lane / TL;
+  const int c = lane % TL;
+  const int n_hg = a.num_kv_heads / HPW;
+  int item = blockIdx.x;
+  const int hg = item % n_hg;
+  item /= n_hg;
+  const int b = item % a.num_seqs;
+  const int j_or_row = item / a.num_seqs;
+  const int g = hg * HPW + hl;
+  const int Hq = a.num_q_heads;
+  const int Hkv = a.num_kv_heads;
+  const int64_t row_bytes = (int64_t)Hkv * D * ELT;
+
+  // This wave's query row, its key range [t0, t1), and the split index.
+  int64_t q_row;
+  int t0, t1, split = 0, nsplit_b = 1, k0 = 0;
+  if constexpr (PREFILL) {
+    const int qb = a.cu_seqlens_q[b];
+    const int lq = a.cu_seqlens_q[b + 1] - qb;
+    const int i = lq - 1 - j_or_row;  // longest rows first
+    if (i < 0) return;
+    k0 = a.cu_seqlens_k[b];
+    const int lk = a.cu_seqlens_k[b + 1] - k0;
+    q_row = qb + i;
+    t0 = 0;
+    t1 = lk - lq + i + 1;
+  } else {
+    const int L = a.context_lens[b];
+    split = j_or_row;
+    q_row = b;
+    t0 = split * a.split_tokens;
+    if (L == 0) {
+      if (split == 0) {  // an empty context gives zeros
+        for (int gq = 0; gq < G; ++gq) {
+          char* op = (char*)a.out + ((q_row * Hq + g * G + gq) * D) * ELT + c * CH;
+          uint32_t z[WPC] = {};
+          for (int jj = 0; jj < NCH; ++jj) store_words<CH>(op + jj * TL * CH, z);
+        }
+      }
+      return;
+    }
+    if (t0 >= L) return;
+    t1 = min(L, t0 + a.split_tokens);
+    nsplit_b = (L + a.split_tokens - 1) / a.split_tokens;
+  }
+
+  // Queries of the G heads sharing KV head g, in this lane's element order.
+  uint32_t qw[G][NW];
+  for (int gq = 0; gq < G; ++gq) {
+    const char* qp = (const char*)a.q + ((q_row * Hq + g * G + gq) * D) * ELT + c * CH;
+    for (int jj = 0; jj < NCH; ++jj) load_words<CH>(&qw[gq][jj * WPC], qp + jj * TL * CH);
+  }
+
+  float m[G], l[G], o[G][DPL];
+  for (int gq = 0; gq < G; ++gq) {
+    m[gq] = kNegInf;
+    l[gq] = 0.f;
+    for (int e = 0; e < DPL; ++e) o[gq][e] = 0.f;
+  }
+
+  const int32_t* table = a.block_tables ? a.block_tables + (int64_t)b * a.max_blocks_per_seq : nullptr;
+  const int bs_mask = (1 << a.log2_block_size) - 1;
+  const char* kbase = (const char*)a.k;
+  const char* vbase = (const char*)a.v;
+  const int lane_off = g * D * ELT + c * CH;
+
+  // Row index of the first token of a step (U tokens never straddle a block:
+  // steps start at multiples of U and U divides the block size).
+  auto step_row = [&](int t) -> int64_t {
+    if (table) {
+      const int64_t blk = uniform(table[t >> a.log2_block_size]);
+      return (blk << a.log2_block_size) + (t & bs_mask);
+    }
+    return (int64_t)k0 + t;
+  };
+
+  struct Buf {
+    uint32_t k[U][NW];
+    uint32_t v[U][NW];
+  };
+  auto load = [&](Buf& buf, int t) {
+    const int64_t r0 = step_row(t);
+    const int last = t1 - 1 - t;  // tokens past the end re-read the last valid row
+    for (int u = 0; u < U; ++u) {
+      const int64_t r = r0 + min(u, last);
+      const char* kp = kbase + r * row_bytes + lane_off;
+      const char* vp = vbase + r * row_bytes + lane_off;
+      for (int jj = 0; jj < NCH; ++jj) {
+        load_words<CH>(&buf.k[u][jj * WPC], kp + jj * TL * CH);
+        load_words<CH>(&buf.v[u][jj * WPC], vp + jj * TL * CH);
+      }
+    }
+  };
+  auto compute = [&](const Buf& buf, int t) {
+    float s[U][G];
+    for (int u = 0; u < U; ++u) {
+      for (int gq = 0; gq < G; ++gq) {
+        float acc = 0.f;
+        for (int w = 0; w < NW; ++w) {
+          if constexpr (BF16) {
+            acc = dot2_bf16(qw[gq][w], buf.k[u][w], acc);
+          } else {
+            acc = fmaf(__uint_as_float(qw[gq][w]), __uint_as_float(buf.k[u][w]), acc);
+          }
+        }
+        s[u][gq] = group_sum<TL>(acc) * a.scale_log2;
+      }
+      if (t + u >= t1)
+        for (int gq = 0; gq < G; ++gq) s[u][gq] = kNegInf;
+    }
+    bool raise = false;
+    float mx[G];
+    for (int gq = 0; gq < G; ++gq) {
+      mx[gq] = s[0][gq];
+      for (int u = 1; u < U; ++u) mx[gq] = fmaxf(mx[gq], s[u][gq]);
+      raise |= mx[gq] > m[gq] + kTau;
+    }
+    if (wave_any(raise)) {
+      for (int gq = 0; gq < G; ++gq) {
+        const float mn = fmaxf(m[gq], mx[gq]);
+        const float alpha = exp2_hw(m[gq] - mn);
+        m[gq] = mn;
+        l[gq] *= alpha;
+        for (int e = 0; e < DPL; ++e) o[gq][e] *= alpha;
+      }
+    }
+    for (int u = 0; u < U; ++u) {
+      float p[G];
+      for (int gq = 0; gq < G; ++gq) {
+        p[gq] = exp2_hw(s[u][gq] - m[gq]);
+        l[gq] += p[gq];
+      }
+      for (int w = 0; w < NW; ++w) {
+        if constexpr (BF16) {
+          const float v0 = bf16_lo(buf.v[u][w]);
+          const float v1 = bf16_hi(buf.v[u][w]);
+          for (int gq = 0; gq < G; ++gq) {
+            o[gq][2 * w] = fmaf(p[gq], v0, o[gq][2 * w]);
+            o[gq][2 * w + 1] = fmaf(p[gq], v1, o[gq][2 * w + 1]);
+          }
+        } else {
+          const float v0 = __uint_as_float(buf.v[u][w]);
+          for (int gq = 0; gq < G; ++gq) o[gq][w] = fmaf(p[gq], v0, o[gq][w]);
+        }
+      }
+    }
+  };
+
+  const int nsteps = (t1 - t0 + U - 1) / U;
+  Buf A, B;
+  load(A, t0);
+  for (int st = 0; st < nsteps; st += 2) {
+    const int ta = t0 + st * U;
+    if (st + 1 < nsteps) load(B, ta + U);
+    compute(A, ta);
+    if (st + 1 >= nsteps) break;
+    if (st + 2 < nsteps) load(A, ta + 2 * U);
+    compute(B, ta + U);
+  }
+
+  if (nsplit_b == 1) {
+    for (int gq = 0; gq < G; ++gq) {
+      const float inv = 1.0f / l[gq];
+      char* op = (char*)a.out + ((q_row * Hq + g * G + gq) * D) * ELT + c * CH;
+      for (int jj = 0; jj < NCH; ++jj) {
+        uint32_t w[WPC];
+        for (int x = 0; x < WPC; ++x) {
+          const int e = (jj * WPC + x) * EPW;
+          if constexpr (BF16) {
+            w[x] = pack_bf16x2(o[gq][e] * inv, o[gq][e + 1] * inv);
+          } else {
+            w[x] = __float_as_uint(o[gq][e] * inv);
+          }
+        }
+        store_words<CH>(op + jj * TL * CH, w);
+      }
+    }
+  } else {
+    const int S = a.num_splits;
+    for (int gq = 0; gq < G; ++gq) {
+      const int64_t slot = ((int64_t)b * Hq + g * G + gq) * S + split;
+      float* wo = a.ws_o + slot * D;
+      for (int jj = 0; jj < NCH; ++jj) {
+        const int d0 = (jj * TL + c) * EPC;
+        for (int x = 0; x < EPC; ++x) wo[d0 + x] = o[gq][jj * EPC + x];
+      }
+      if (c == 0) {
+        a.ws_ml[slot * 2] = m[gq];
+        a.ws_ml[slot * 2 + 1] = l[gq];
+      }
+    }
+  }
+}
+
+// Merge the split states of each (sequence, query head): M = max_j m_j,
+// w_j = 2^(m_j - M), out = sum_j w_j o_j / sum_j w_j l_j.  One wave per pair,
+// splits merged in index order.
+template <bool BF16, int D>
+__global__ __launch_bounds__(256) void decode_reduce_kernel(RowAttnArgs a) {
+  constexpr int EPL = D / 64;  // elements per lane
+  const int pair = blockIdx.x * 4 + threadIdx.x / 64;
+  const int lane = threadIdx.x % 64;
+  const int Hq = a.num_q_heads;
+  if (pair >= a.num_seqs * Hq) return;
+  const int b = pair / Hq;
+  const int L = a.context_lens[b];
+  const int ns = (L + a.split_tokens - 1) / a.split_tokens;
+  if (ns <= 1) return;
+  const int S = a.num_splits;
+  const float* ml = a.ws_ml + (int64_t)pair * S * 2;
+  const float* wo = a.ws_o + (int64_t)pair * S * D + lane * EPL;
+  float M = kNegInf;
+  for (int j = 0; j < ns; ++j) M = fmaxf(M, ml[2 * j]);
+  float den = 0.f, acc[EPL] = {};
+  for (int j = 0; j < ns; ++j) {
+    const float w = exp2_hw(ml[2 * j] - M);
+    den = fmaf(w, ml[2 * j + 1], den);
+    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(w, wo[(int64_t)j * D + e], acc[e]);
+  }
+  const float inv = 1.0f / den;
+  if constexpr (BF16) {
+    uint16_t* op = (uint16_t*)a.out + (int64_t)pair * D + lane * EPL;
+    if constexpr (EPL == 2) {
+      *reinterpret_cast<uint32_t*>(op) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    } else {
+      op[0] = (uint16_t)(pack_bf16x2(acc[0] * inv, 0.f) & 0xffffu);
+    }
+  } else {
+    float* op = (float*)a.out + (int64_t)pair * D + lane * EPL;
+    for (int e = 0; e < EPL; ++e) op[e] = acc[e] * inv;
+  }
+}
+
+}  // namespace pkv

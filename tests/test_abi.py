@@ -1,0 +1,100 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every
+function include/pkv.h declares, and rejects bad arguments before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_gqa_mapping_amd as pkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(pkv.library_path), reason="libpkv.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pkv_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_operations():
+    names = declared_functions()
+    for n in ("pkv_kv_store", "pkv_paged_decode_attn", "pkv_paged_prefill_attn"):
+        assert n in names
+
+
+@needs_lib
+def test_library_exports_every_declared_function():
+    L = ctypes.CDLL(pkv.library_path)
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+@needs_lib
+def test_status_strings_and_version():
+    L = pkv.lib()
+    assert L.pkv_version() >= 100
+    for code, name in [(0, "PKV_OK"), (-1, "PKV_ERR_INVALID_ARG"), (-2, "PKV_ERR_UNSUPPORTED"),
+                       (-3, "PKV_ERR_WORKSPACE"), (-4, "PKV_ERR_HIP")]:
+        assert L.pkv_status_string(code).decode() == name
+
+
+def _dec(L, **kw):
+    args = dict(q=1 << 20, k=1 << 20, v=1 << 20, bt=1 << 20, W=4, cl=1 << 20, maxL=1000, scale=0.1, out=1 << 20,
+                B=2, Hq=32, Hkv=8, D=128, NB=10, bs=256, dtype=1, split=0, ws=None, ws_bytes=0)
+    args.update(kw)
+    a = args
+    return L.pkv_paged_decode_attn(a["q"], a["k"], a["v"], a["bt"], a["W"], a["cl"], a["maxL"], a["scale"], a["out"],
+                                   a["B"], a["Hq"], a["Hkv"], a["D"], a["NB"], a["bs"], a["dtype"], a["split"],
+                                   a["ws"], a["ws_bytes"], None)
+
+
+@needs_lib
+def test_decode_argument_errors_before_launch():
+    L = pkv.lib()
+    assert _dec(L, D=96) == -2
+    assert _dec(L, bs=48) == -2
+    assert _dec(L, Hq=24) == -2            # group size 3
+    assert _dec(L, Hq=30) == -1            # not a multiple of Hkv
+    assert _dec(L, q=None) == -1
+    assert _dec(L, q=(1 << 20) + 8) == -1  # misaligned
+    assert _dec(L, maxL=2000) == -1        # beyond W * bs
+    assert _dec(L, split=100) == -1        # not a multiple of 64
+    assert _dec(L, maxL=1000, split=64) == -3   # needs a workspace
+    assert "workspace" in L.pkv_last_error().decode()
+    assert _dec(L, B=0) == 0               # nothing to do
+    assert _dec(L, dtype=7) == -2
+
+
+@needs_lib
+def test_workspace_and_split_queries():
+    L = pkv.lib()
+    assert L.pkv_decode_workspace_bytes(4, 8, 128, 100, 128) == 0
+    assert L.pkv_decode_workspace_bytes(4, 8, 128, 300, 128) == 4 * 8 * 3 * 130 * 4
+    for B, Hkv, maxL in [(256, 8, 1024), (64, 8, 8192), (200, 8, 32768), (4, 2, 100), (1, 1, 1)]:
+        s = L.pkv_decode_split_tokens(B, Hkv * 4, Hkv, 128, maxL, 256, 1)
+        assert s > 0 and s % 64 == 0
+
+
+@needs_lib
+def test_kv_store_and_prefill_argument_errors():
+    L = pkv.lib()
+    P = 1 << 20
+    assert L.pkv_kv_store(P, P, P, P, P, -1, 8, 128, 10, 256, 1, None) == -1
+    assert L.pkv_kv_store(P, P, P, P, P, 0, 8, 128, 10, 256, 1, None) == 0
+    assert L.pkv_kv_store(P, P, P, P, None, 4, 8, 128, 10, 256, 1, None) == -1
+    assert L.pkv_kv_store(P, P, P, P, P, 4, 8, 128, 10, 100, 1, None) == -2
+    # prefill: max_seqlen_q > max_seqlen_k, and a table too narrow for max_seqlen_k
+    assert L.pkv_paged_prefill_attn(P, P, P, P, P, P, 4, P, 0.0, 2, 10, 9, 8, 32, 8, 128, 10, 256, 1, None) == -1
+    assert L.pkv_paged_prefill_attn(P, P, P, P, P, P, 1, P, 0.0, 2, 10, 9, 300, 32, 8, 128, 10, 256, 1, None) == -1
+    assert L.pkv_paged_prefill_attn(P, P, P, P, P, P, 4, P, 0.0, 0, 0, 0, 0, 32, 8, 128, 10, 256, 1, None) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(pkv, "library_path", "/nonexistent/libpkv.so")
+    monkeypatch.setattr(pkv, "_lib", None)
+    with pytest.raises(pkv.PkvError):
+        pkv.lib()
