@@ -69,16 +69,18 @@ int check_heads(int32_t num_q_heads, int32_t num_kv_heads) {
 
 int32_t round_up(int64_t x, int32_t m) { return (int32_t)(((x + m - 1) / m) * m); }
 
-// Split length for decode (tokens, multiple of 64): aim for ~4096 waves over
-// the grid so that every CU has work to hide latency with, but keep splits at
-// least 256 tokens long so the partial states stay small next to the KV bytes.
+// Split length for decode (tokens): a power of two of at least 256, the
+// smallest that keeps the grid near 4096 waves (16 per CU), so that every CU
+// has work while the per-split partial states stay small next to the K/V
+// bytes they summarise.  A context of at most 256 tokens is one split.
 int32_t auto_split(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
   if (max_context_len <= 256) return round_up(std::max(max_context_len, 1), 64);
   const int64_t base = (int64_t)num_seqs * std::max(1, num_kv_heads / 8);
   const int64_t want_splits = std::max<int64_t>(1, (4096 + base - 1) / base);
-  int32_t split = round_up((max_context_len + want_splits - 1) / want_splits, 64);
-  split = std::max(split, 256);
-  return std::min(split, round_up(max_context_len, 64));
+  const int64_t need = (max_context_len + want_splits - 1) / want_splits;
+  int32_t split = 256;
+  while (split < need && split < max_context_len) split *= 2;
+  return split;
 }
 
 struct DecodeCall {

@@ -38,7 +38,7 @@ __device__ __forceinline__ int vt_column(int k) {
 }
 
 template <int D, int HW>
-__global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int PB = 4 / HW;           // 32-position blocks per workgroup
   constexpr int QP = 32 * PB;          // positions per workgroup
   constexpr int KSTEPS = D / 16;       // contraction steps of Q K^T
@@ -46,8 +46,10 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int KS = D + 8;            // LDS K row stride (elements): 16-byte pad
   constexpr int VS = kKT + 8;          // LDS V^T row stride (elements)
   constexpr int CPR = D / 8;           // 16-byte chunks per K/V row
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[kKT * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[D * VS];
+  constexpr int CPT = CPR / 4;         // K chunks per thread (4 threads per K row)
+  constexpr int VT = (kKT / 4) * CPR;  // threads that load V (4 keys x 8 dims each)
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kKT * KS];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][D * VS];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -99,20 +101,93 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
     }
   }
 
+  // Tile loads.  K: thread t owns row (t % 16) + 16 (t / 64) and chunks
+  // ((t / 16) % 4) + 4 i, so 16 consecutive lanes write one chunk of 16
+  // consecutive rows (the row stride keeps them on distinct banks) and each
+  // global load instruction reads 64 contiguous bytes of 16 rows.  V: thread t
+  // owns keys 4 (t % 16) .. +3 and dims 8 (t / 16) .. +7, so 16 consecutive
+  // lanes write the 16 eight-byte key slots of one V^T row (128 contiguous
+  // bytes).
   const int32_t* table = a.block_tables ? a.block_tables + (int64_t)b * a.max_blocks_per_seq : nullptr;
-  const int bs_mask = (1 << a.log2_block_size) - 1;
+  const int lbs = a.log2_block_size;
+  const int bs_mask = (1 << lbs) - 1;
   const uint16_t* kbase = (const uint16_t*)a.k;
   const uint16_t* vbase = (const uint16_t*)a.v;
-  // element offset of key t's row for KV head g
-  auto row_elem = [&](int t) -> int64_t {
-    int64_t r;
-    if (table) {
-      const int64_t blk = table[t >> a.log2_block_size];
-      r = (blk << a.log2_block_size) + (t & bs_mask);
-    } else {
-      r = (int64_t)k0 + t;
+  const int k_row = (tid & 15) + 16 * (tid >> 6);
+  const int k_c0 = (tid >> 4) & 3;
+  const bool v_loader = uniform(wave) < VT / 64;  // whole waves (VT is a multiple of 64)
+  const int v_kg = tid & 15;
+  const int v_dc = tid >> 4;
+
+  // Keys past the end of the sequence (the tail of the last tile) re-read the
+  // last key's row: their scores are masked (key > every position) and their
+  // weights are exactly 0, so finite data suffices and no zero fill is needed.
+  const int last_key = Lk - 1;
+  // block id holding key t (packed K/V: unused)
+  auto block_id = [&](int t) -> int32_t { return table ? table[min(t, last_key) >> lbs] : 0; };
+  // element offset of key tc's row (tc <= last_key) for KV head g; blk is the block holding tc
+  const int row_stride = Hkv * D;
+  const int64_t blk_stride = (int64_t)row_stride << lbs;
+  const int head_off = g * D;
+  auto row_elem = [&](int tc, int32_t blk) -> int64_t {
+    if (table) return (int64_t)blk * blk_stride + ((tc & bs_mask) * row_stride + head_off);
+    return (int64_t)(k0 + tc) * row_stride + head_off;
+  };
+
+  static_assert(CPT == 2 || CPT == 4, "head_dim 64 or 128");
+  // prefetched rows, as separate values so that they stay in registers
+  uint4 k0r, k1r, k2r, k3r;  // K chunks k_c0 + 4 i, i < CPT
+  uint4 v0, v1, v2, v3;      // V rows of keys 4 kg .. 4 kg + 3
+  auto issue_loads = [&](int kt, int32_t bk, int32_t bv) {
+    const int64_t ek = row_elem(min(kt * kKT + k_row, last_key), bk) + k_c0 * 8;
+    k0r = *reinterpret_cast<const uint4*>(kbase + ek);
+    k1r = *reinterpret_cast<const uint4*>(kbase + ek + 32);
+    if constexpr (CPT == 4) {
+      k2r = *reinterpret_cast<const uint4*>(kbase + ek + 64);
+      k3r = *reinterpret_cast<const uint4*>(kbase + ek + 96);
     }
-    return (r * Hkv + g) * D;
+    if (v_loader) {
+      // the 4 keys are consecutive rows of one block (4-aligned, block_size >= 8);
+      // keys past the end all read the last key's row
+      const int tv = kt * kKT + 4 * v_kg;
+      const int tvc = min(tv, last_key);
+      const int64_t ev = row_elem(tvc, bv) + v_dc * 8;
+      auto row = [&](int i) {
+        return *reinterpret_cast<const uint4*>(vbase + ev + (int64_t)((min(tv + i, last_key) - tvc) * row_stride));
+      };
+      v0 = row(0);
+      v1 = row(1);
+      v2 = row(2);
+      v3 = row(3);
+    }
+  };
+  auto write_lds = [&](int buf) {
+    uint16_t* kd = &lds_k[buf][k_row * KS + k_c0 * 8];
+    *reinterpret_cast<uint4*>(kd) = k0r;
+    *reinterpret_cast<uint4*>(kd + 32) = k1r;
+    if constexpr (CPT == 4) {
+      *reinterpret_cast<uint4*>(kd + 64) = k2r;
+      *reinterpret_cast<uint4*>(kd + 96) = k3r;
+    }
+    if (v_loader) {
+      const int vc = vt_column(4 * v_kg);
+      const uint32_t r0[4] = {v0.x, v0.y, v0.z, v0.w};
+      const uint32_t r1[4] = {v1.x, v1.y, v1.z, v1.w};
+      const uint32_t r2[4] = {v2.x, v2.y, v2.z, v2.w};
+      const uint32_t r3[4] = {v3.x, v3.y, v3.z, v3.w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int d = v_dc * 8 + 2 * w;
+        // v_perm_b32: selector bytes 0-3 pick from the second operand, 4-7 from the first
+        uint2 lo, hi;
+        lo.x = __builtin_amdgcn_perm(r1[w], r0[w], 0x05040100u);  // (key 0, key 1) of dim d
+        lo.y = __builtin_amdgcn_perm(r3[w], r2[w], 0x05040100u);  // (key 2, key 3)
+        hi.x = __builtin_amdgcn_perm(r1[w], r0[w], 0x07060302u);  // dim d + 1
+        hi.y = __builtin_amdgcn_perm(r3[w], r2[w], 0x07060302u);
+        *reinterpret_cast<uint2*>(&lds_v[buf][d * VS + vc]) = lo;
+        *reinterpret_cast<uint2*>(&lds_v[buf][(d + 1) * VS + vc]) = hi;
+      }
+    }
   };
 
   f32x16_t acc_o[MD];
@@ -120,77 +195,36 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
     for (int r = 0; r < 16; ++r) acc_o[md][r] = 0.f;
   float m = kNegInf;  // running reference max of this lane's column (log2 units)
   float lsum = 0.f;   // this half-wave's share of the column's weight sum
+  const float c = a.scale_log2;  // > 0
   const uint32_t kOnes = 0x3F803F80u;  // bf16 pair (1, 1)
 
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int key0 = kt * kKT;
-    __syncthreads();
-    // K tile, row-major: chunk id -> (row, 16-byte chunk).
-    for (int idc = tid; idc < kKT * CPR; idc += 256) {
-      const int row = idc / CPR;
-      const int ch = idc % CPR;
-      const int t = key0 + row;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (t < Lk) x = *reinterpret_cast<const uint4*>(kbase + row_elem(t) + ch * 8);
-      *reinterpret_cast<uint4*>(&lds_k[row * KS + ch * 8]) = x;
-    }
-    // V tile, transposed: 4 keys x 8 dims per thread.
-    if (tid < (kKT / 4) * CPR) {
-      const int kg = tid / CPR;
-      const int dc = tid % CPR;
-      uint4 r[4];
-      for (int i = 0; i < 4; ++i) {
-        const int t = key0 + kg * 4 + i;
-        r[i] = make_uint4(0, 0, 0, 0);
-        if (t < Lk) r[i] = *reinterpret_cast<const uint4*>(vbase + row_elem(t) + dc * 8);
-      }
-      const int vc = vt_column(kg * 4);
-      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[0]);
-      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[1]);
-      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[2]);
-      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r[3]);
-      for (int w = 0; w < 4; ++w) {
-        const int d = dc * 8 + 2 * w;
-        uint2 lo, hi;
-        lo.x = (w0[w] & 0xffffu) | (w1[w] << 16);
-        lo.y = (w2[w] & 0xffffu) | (w3[w] << 16);
-        hi.x = (w0[w] >> 16) | (w1[w] & 0xffff0000u);
-        hi.y = (w2[w] >> 16) | (w3[w] & 0xffff0000u);
-        *reinterpret_cast<uint2*>(&lds_v[d * VS + vc]) = lo;
-        *reinterpret_cast<uint2*>(&lds_v[(d + 1) * VS + vc]) = hi;
-      }
-    }
-    __syncthreads();
-    if (!wave_active || key0 > w_max_pos) continue;
-
-    // S^T = K Q^T
+  auto compute = [&](int buf, int key0) {
+    // S^T = K Q^T (raw scores)
     f32x16_t acc_s[2];
     for (int mb = 0; mb < 2; ++mb)
       for (int r = 0; r < 16; ++r) acc_s[mb][r] = 0.f;
     for (int kk = 0; kk < KSTEPS; ++kk) {
       for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8_t af =
-            __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&lds_k[(mb * 32 + col) * KS + 16 * kk + 8 * half]));
+        const bf16x8_t af = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const uint4*>(&lds_k[buf][(mb * 32 + col) * KS + 16 * kk + 8 * half]));
         acc_s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[kk], acc_s[mb], 0, 0, 0);
       }
     }
-
-    // online softmax over this tile's keys for this lane's column
-    const bool diag = key0 + kKT - 1 > w_min_pos;
-    float s[32];
-    float mx = kNegInf;
-    for (int mb = 0; mb < 2; ++mb) {
-      for (int r = 0; r < 16; ++r) {
-        float v = acc_s[mb][r] * a.scale_log2;
-        if (diag) {
-          const int key = key0 + mb * 32 + (r >> 2) * 8 + half * 4 + (r & 3);
-          if (key > pos) v = kNegInf;
-        }
-        s[mb * 16 + r] = v;
-        mx = fmaxf(mx, v);
-      }
+    // causal mask (only on tiles that reach past the wave's first position):
+    // key key0 + off(r) with off(r) = mb*32 + (r/4)*8 + half*4 + r%4 is
+    // visible iff off(r) - half*4 <= pos - key0 - half*4
+    if (key0 + kKT - 1 > w_min_pos) {
+      const int lim = pos - key0 - half * 4;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (mb * 32 + (r >> 2) * 8 + (r & 3) > lim) acc_s[mb][r] = kNegInf;
     }
-    mx = halves_max(mx);
+    float mx = kNegInf;
+    for (int mb = 0; mb < 2; ++mb)
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc_s[mb][r]);
+    mx = halves_max(mx) * c;  // c > 0, so the max commutes with the scaling
     if (wave_any(mx > m + kTau)) {
       const float mn = fmaxf(m, mx);
       const float alpha = exp2_hw(m - mn);
@@ -199,21 +233,59 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
       for (int md = 0; md < MD; ++md)
         for (int r = 0; r < 16; ++r) acc_o[md][r] *= alpha;
     }
+    // P^T = 2^(c s - m), rounded to bf16, as the B operand of the four 16-key steps
     uint32_t pw[16];
     for (int i = 0; i < 16; ++i) {
-      pw[i] = pack_bf16x2(exp2_hw(s[2 * i] - m), exp2_hw(s[2 * i + 1] - m));
+      const float s0 = acc_s[i >> 3][(2 * i) & 15];
+      const float s1 = acc_s[i >> 3][(2 * i + 1) & 15];
+      pw[i] = pack_bf16x2(exp2_hw(fmaf(s0, c, -m)), exp2_hw(fmaf(s1, c, -m)));
       lsum = dot2_bf16(pw[i], kOnes, lsum);
     }
-
     // O^T += V^T P^T
     for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8_t bf = __builtin_bit_cast(bf16x8_t, make_uint4(pw[4 * ks], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]));
+      const bf16x8_t bf =
+          __builtin_bit_cast(bf16x8_t, make_uint4(pw[4 * ks], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]));
       for (int md = 0; md < MD; ++md) {
-        const bf16x8_t af =
-            __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(&lds_v[(md * 32 + col) * VS + 16 * ks + 8 * half]));
+        const bf16x8_t af = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const uint4*>(&lds_v[buf][(md * 32 + col) * VS + 16 * ks + 8 * half]));
         acc_o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc_o[md], 0, 0, 0);
       }
     }
+  };
+
+  // Pipeline: tile kt+1's global loads are in flight while tile kt is computed
+  // from LDS; block ids run two tiles ahead.  One barrier per tile.  The
+  // tiles past this wave's last position are only loaded for the other waves
+  // (second loop), which keeps the compute loop free of a data-dependent skip.
+  int32_t bk = block_id(k_row), bv = block_id(4 * v_kg);
+  issue_loads(0, bk, bv);
+  if (n_kt > 1) {
+    bk = block_id(kKT + k_row);
+    bv = block_id(kKT + 4 * v_kg);
+  }
+  write_lds(0);
+  __syncthreads();
+  auto advance = [&](int kt) {
+    if (kt + 1 < n_kt) {
+      issue_loads(kt + 1, bk, bv);
+      if (kt + 2 < n_kt) {
+        bk = block_id((kt + 2) * kKT + k_row);
+        bv = block_id((kt + 2) * kKT + 4 * v_kg);
+      }
+    }
+  };
+  const int n_kt_wave = wave_active ? min(n_kt, w_max_pos / kKT + 1) : 0;
+  int kt = 0;
+  for (; kt < n_kt_wave; ++kt) {
+    advance(kt);
+    compute(kt & 1, kt * kKT);
+    if (kt + 1 < n_kt) write_lds((kt & 1) ^ 1);
+    __syncthreads();
+  }
+  for (; kt < n_kt; ++kt) {
+    advance(kt);
+    if (kt + 1 < n_kt) write_lds((kt & 1) ^ 1);
+    __syncthreads();
   }
 
   if (!wave_active || !col_valid) return;

@@ -2,6 +2,24 @@
 // decode reduce, fp32 prefill rows).
 #include "row_attn.hpp"
 
+// Compile-time tuning knobs (defaults are the measured choice):
+//   PKV_ROW_HPW_MAX  cap on KV heads per wave (8, 4, 2 or 1)
+//   PKV_ROW_MAX_ACC  cap on fp32 output accumulators per lane, G * D / (64 / hpw)
+//   PKV_ROW_U        tokens per step (0: 4 for bf16 with G <= 2, else 2)
+//   PKV_ROW_R        step buffers in the load ring (R - 1 steps in flight)
+#ifndef PKV_ROW_HPW_MAX
+#define PKV_ROW_HPW_MAX 8
+#endif
+#ifndef PKV_ROW_MAX_ACC
+#define PKV_ROW_MAX_ACC 64
+#endif
+#ifndef PKV_ROW_U
+#define PKV_ROW_U 0
+#endif
+#ifndef PKV_ROW_R
+#define PKV_ROW_R 4
+#endif
+
 namespace pkv {
 
 namespace {
@@ -15,24 +33,24 @@ int choose_hpw(int32_t dtype, int32_t head_dim, int32_t num_q_heads, int32_t num
   const int G = num_q_heads / num_kv_heads;
   int fallback = 0;
   for (int hpw : {8, 4, 2, 1}) {
-    if (num_kv_heads % hpw) continue;
+    if (hpw > PKV_ROW_HPW_MAX || num_kv_heads % hpw) continue;
     const int dpl = head_dim / (64 / hpw);
     if (dpl * elt < 4) continue;
     fallback = hpw;
-    if (G * dpl <= 64) return hpw;
+    if (G * dpl <= PKV_ROW_MAX_ACC) return hpw;
   }
   return fallback;
 }
 
 template <bool BF16, int D, int HPW, int G, bool PREFILL>
 hipError_t launch_one(const RowAttnArgs& a, hipStream_t stream) {
-  constexpr int U = (BF16 && G <= 2) ? 4 : 2;  // tokens per step
+  constexpr int U = PKV_ROW_U ? PKV_ROW_U : ((BF16 && G <= 2) ? 4 : 2);  // tokens per step
   const int n_hg = a.num_kv_heads / HPW;
   const int64_t rows = PREFILL ? (int64_t)a.max_rows : (int64_t)a.num_splits;
   const int64_t blocks = (int64_t)n_hg * a.num_seqs * rows;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((row_attn_kernel<BF16, D, HPW, G, U, PREFILL>), dim3((unsigned)blocks), dim3(64), 0, stream, a);
+  hipLaunchKernelGGL((row_attn_kernel<BF16, D, HPW, G, U, PKV_ROW_R, PREFILL>), dim3((unsigned)blocks), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -19,7 +19,9 @@
 // pairs), an all-reduce over the TL lanes of the group with DPP, the online
 // softmax update (max in log2 units; the running reference max is only raised
 // when a score exceeds it by more than kTau, which keeps the weights <= 2^kTau
-// and skips most rescales), then weights times V accumulated in fp32.
+// and skips most rescales), then weights times V accumulated in fp32.  For
+// bf16 the weights are rounded to bf16 and two tokens go through one v_dot2
+// per element; the weight sum is taken over the same rounded weights.
 #pragma once
 
 #include "common.hpp"
@@ -69,7 +71,7 @@ __device__ __forceinline__ void store_words(char* p, const uint32_t* w) {
   *reinterpret_cast<T*>(p) = x;
 }
 
-template <bool BF16, int D, int HPW, int G, int U, bool PREFILL>
+template <bool BF16, int D, int HPW, int G, int U, int R, bool PREFILL>
 __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
   constexpr int ELT = BF16 ? 2 : 4;
   constexpr int TL = 64 / HPW;
@@ -131,10 +133,19 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
   }
 
   // Queries of the G heads sharing KV head g, in this lane's element order.
+  // Scores are scaled by c >= 0 (a negative scale is applied by negating q,
+  // which is exact, and using |c|).
   uint32_t qw[G][NW];
   for (int gq = 0; gq < G; ++gq) {
     const char* qp = (const char*)a.q + ((q_row * Hq + g * G + gq) * D) * ELT + c * CH;
     for (int jj = 0; jj < NCH; ++jj) load_words<CH>(&qw[gq][jj * WPC], qp + jj * TL * CH);
+  }
+  float cs = a.scale_log2;
+  if (cs < 0.f) {
+    const uint32_t sign = BF16 ? 0x80008000u : 0x80000000u;
+    for (int gq = 0; gq < G; ++gq)
+      for (int w = 0; w < NW; ++w) qw[gq][w] ^= sign;
+    cs = -cs;
   }
 
   float m[G], l[G], o[G][DPL];
@@ -151,10 +162,21 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
   const int lane_off = g * D * ELT + c * CH;
 
   // Row index of the first token of a step (U tokens never straddle a block:
-  // steps start at multiples of U and U divides the block size).
+  // steps start at multiples of U and U divides the block size).  Block ids
+  // come from a 64-entry window of the table held one per lane and read with
+  // readlane, so a lookup costs no memory round trip; the window moves when a
+  // step leaves it.
+  int win0 = -1 << 30;  // first block index of the window
+  int win = 0;          // this lane's entry: table[win0 + lane]
   auto step_row = [&](int t) -> int64_t {
     if (table) {
-      const int64_t blk = uniform(table[t >> a.log2_block_size]);
+      const int bi = t >> a.log2_block_size;
+      if (bi - win0 >= 64 || bi < win0) {
+        win0 = bi;
+        const int e = bi + lane;
+        win = e < a.max_blocks_per_seq ? table[e] : 0;
+      }
+      const int64_t blk = __builtin_amdgcn_readlane(win, bi - win0);
       return (blk << a.log2_block_size) + (t & bs_mask);
     }
     return (int64_t)k0 + t;
@@ -177,11 +199,16 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
       }
     }
   };
+  static_assert(!BF16 || U % 2 == 0, "bf16 steps pair tokens");
+  const uint32_t kOnes = 0x3F803F80u;  // bf16 pair (1, 1)
   auto compute = [&](const Buf& buf, int t) {
     float s[U][G];
+#pragma unroll
     for (int u = 0; u < U; ++u) {
+#pragma unroll
       for (int gq = 0; gq < G; ++gq) {
         float acc = 0.f;
+#pragma unroll
         for (int w = 0; w < NW; ++w) {
           if constexpr (BF16) {
             acc = dot2_bf16(qw[gq][w], buf.k[u][w], acc);
@@ -189,59 +216,104 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
             acc = fmaf(__uint_as_float(qw[gq][w]), __uint_as_float(buf.k[u][w]), acc);
           }
         }
-        s[u][gq] = group_sum<TL>(acc) * a.scale_log2;
+        s[u][gq] = group_sum<TL>(acc) * cs;
       }
-      if (t + u >= t1)
-        for (int gq = 0; gq < G; ++gq) s[u][gq] = kNegInf;
+    }
+    // tokens past the end (last step only): they take token 0's score for the
+    // max and get weight 0 below
+    const int nvalid = t1 - t;
+    if (nvalid < U) {
+#pragma unroll
+      for (int u = 1; u < U; ++u)
+        if (u >= nvalid)
+#pragma unroll
+          for (int gq = 0; gq < G; ++gq) s[u][gq] = s[0][gq];
     }
     bool raise = false;
     float mx[G];
+#pragma unroll
     for (int gq = 0; gq < G; ++gq) {
       mx[gq] = s[0][gq];
+#pragma unroll
       for (int u = 1; u < U; ++u) mx[gq] = fmaxf(mx[gq], s[u][gq]);
       raise |= mx[gq] > m[gq] + kTau;
     }
     if (wave_any(raise)) {
+#pragma unroll
       for (int gq = 0; gq < G; ++gq) {
         const float mn = fmaxf(m[gq], mx[gq]);
         const float alpha = exp2_hw(m[gq] - mn);
         m[gq] = mn;
         l[gq] *= alpha;
+#pragma unroll
         for (int e = 0; e < DPL; ++e) o[gq][e] *= alpha;
       }
     }
-    for (int u = 0; u < U; ++u) {
-      float p[G];
-      for (int gq = 0; gq < G; ++gq) {
-        p[gq] = exp2_hw(s[u][gq] - m[gq]);
-        l[gq] += p[gq];
-      }
-      for (int w = 0; w < NW; ++w) {
-        if constexpr (BF16) {
-          const float v0 = bf16_lo(buf.v[u][w]);
-          const float v1 = bf16_hi(buf.v[u][w]);
+    float p[U][G];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int gq = 0; gq < G; ++gq) p[u][gq] = exp2_hw(s[u][gq] - m[gq]);  // the max token gets exactly 1
+    if (nvalid < U) {
+#pragma unroll
+      for (int u = 1; u < U; ++u)
+        if (u >= nvalid)
+#pragma unroll
+          for (int gq = 0; gq < G; ++gq) p[u][gq] = 0.f;
+    }
+    if constexpr (BF16) {
+      // weights of two tokens as one bf16 pair; V of the two tokens interleaved
+      // per element, so each v_dot2 adds both tokens' terms of one element.
+#pragma unroll
+      for (int u = 0; u < U; u += 2) {
+        uint32_t pp[G];
+#pragma unroll
+        for (int gq = 0; gq < G; ++gq) {
+          pp[gq] = pack_bf16x2(p[u][gq], p[u + 1][gq]);
+          l[gq] = dot2_bf16(pp[gq], kOnes, l[gq]);
+        }
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const uint32_t a0 = buf.v[u][w], a1 = buf.v[u + 1][w];
+          const uint32_t lo = (a0 & 0xffffu) | (a1 << 16);
+          const uint32_t hi = (a0 >> 16) | (a1 & 0xffff0000u);
+#pragma unroll
           for (int gq = 0; gq < G; ++gq) {
-            o[gq][2 * w] = fmaf(p[gq], v0, o[gq][2 * w]);
-            o[gq][2 * w + 1] = fmaf(p[gq], v1, o[gq][2 * w + 1]);
+            o[gq][2 * w] = dot2_bf16(pp[gq], lo, o[gq][2 * w]);
+            o[gq][2 * w + 1] = dot2_bf16(pp[gq], hi, o[gq][2 * w + 1]);
           }
-        } else {
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int gq = 0; gq < G; ++gq) l[gq] += p[u][gq];
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
           const float v0 = __uint_as_float(buf.v[u][w]);
-          for (int gq = 0; gq < G; ++gq) o[gq][w] = fmaf(p[gq], v0, o[gq][w]);
+#pragma unroll
+          for (int gq = 0; gq < G; ++gq) o[gq][w] = fmaf(p[u][gq], v0, o[gq][w]);
         }
       }
     }
   };
 
+  // A ring of R step buffers: the loads of step s + R - 1 are issued before
+  // step s is computed, so R - 1 steps of K/V rows are in flight per wave.
   const int nsteps = (t1 - t0 + U - 1) / U;
-  Buf A, B;
-  load(A, t0);
-  for (int st = 0; st < nsteps; st += 2) {
-    const int ta = t0 + st * U;
-    if (st + 1 < nsteps) load(B, ta + U);
-    compute(A, ta);
-    if (st + 1 >= nsteps) break;
-    if (st + 2 < nsteps) load(A, ta + 2 * U);
-    compute(B, ta + U);
+  Buf ring[R];
+#pragma unroll
+  for (int r = 0; r < R - 1; ++r)
+    if (r < nsteps) load(ring[r], t0 + r * U);
+  for (int st = 0; st < nsteps; st += R) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int s = st + r;
+      if (s >= nsteps) break;
+      if (s + R - 1 < nsteps) load(ring[(r + R - 1) % R], t0 + (s + R - 1) * U);
+      compute(ring[r], t0 + s * U);
+    }
   }
 
   if (nsplit_b == 1) {
