@@ -24,6 +24,51 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_traffic.md")
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the HIP/C++ sources of libpkv.so (name + bytes, sorted)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "paged_kv_gqa_mapping_amd", "csrc")
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
+            h.update(name.encode())
+            h.update(open(os.path.join(d, name), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per decode-split launch from the committed counter summary, or None when
+    the kernel sources changed since the counters were taken (or no summary exists)."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    fields = dict(line.strip("- `").split(": ", 1) for line in text.splitlines()
+                  if line.startswith("- `") and ": " in line)
+    try:
+        if fields.get("kernel_source_sha256", "").strip("`") != kernel_source_hash():
+            return None
+        return int(fields["hbm_bytes_per_launch"].strip("`"))
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy(mib: int) -> None:
+    """A plain device-to-device copy of a known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+
+    n = mib << 20
+    x = torch.empty(n, dtype=torch.uint8, device="cuda")
+    x.fill_(3)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration_copy_bytes": n, "launches": 3}), flush=True)
 
 
 def log(msg):
@@ -67,6 +112,8 @@ def main():
     ap.add_argument("--workload", type=int, default=5, help="workload number (5 = the mixed step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -81,6 +128,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     pkv.lib()  # fail loudly if the library is missing
 
     t_build = time.perf_counter()
@@ -170,8 +220,9 @@ def main():
                               "frac_mfma": round(tfs / MFMA_BF16_PEAK_TFS, 4), "tflop": round(flops / 1e12, 5)}
     if has_dec:
         value = kv_bytes / (ms_per_step * 1e-3) / 1e9
+        traffic = measured_traffic() if args.workload == 5 and not args.split_tokens else None
         roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                    "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                     "kernel": "row_attn_kernel (decode split pass)",
                     "algorithmic_bytes_per_launch": int(split_bytes)}
     else:
