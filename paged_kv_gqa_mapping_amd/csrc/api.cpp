@@ -69,16 +69,17 @@ int check_heads(int32_t num_q_heads, int32_t num_kv_heads) {
 
 int32_t round_up(int64_t x, int32_t m) { return (int32_t)(((x + m - 1) / m) * m); }
 
-// Split length for decode (tokens): a power of two of at least 256, the
-// smallest that keeps the grid near 4096 waves (16 per CU), so that every CU
-// has work while the per-split partial states stay small next to the K/V
-// bytes they summarise.  A context of at most 256 tokens is one split.
+// Split length for decode (tokens): a power of two, the smallest that keeps
+// the grid near 4096 waves (16 per CU) so that every CU has work, but at
+// least 512 tokens (256 when the longest context is at most 1024) so that a
+// wave's fixed costs (first loads, partial-state write) stay small next to
+// its streaming time.  A context of at most 256 tokens is one split.
 int32_t auto_split(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
   if (max_context_len <= 256) return round_up(std::max(max_context_len, 1), 64);
   const int64_t base = (int64_t)num_seqs * std::max(1, num_kv_heads / 8);
   const int64_t want_splits = std::max<int64_t>(1, (4096 + base - 1) / base);
   const int64_t need = (max_context_len + want_splits - 1) / want_splits;
-  int32_t split = 256;
+  int32_t split = max_context_len <= 1024 ? 256 : 512;
   while (split < need && split < max_context_len) split *= 2;
   return split;
 }

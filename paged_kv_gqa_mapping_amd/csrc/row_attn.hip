@@ -5,7 +5,7 @@
 // Compile-time tuning knobs (defaults are the measured choice):
 //   PKV_ROW_HPW_MAX  cap on KV heads per wave (8, 4, 2 or 1)
 //   PKV_ROW_MAX_ACC  cap on fp32 output accumulators per lane, G * D / (64 / hpw)
-//   PKV_ROW_U        tokens per step (0: 4 for bf16 with G <= 2, else 2)
+//   PKV_ROW_U        tokens per step (0: 4 for bf16 with G <= 4, else 2)
 //   PKV_ROW_R        step buffers in the load ring (R - 1 steps in flight)
 #ifndef PKV_ROW_HPW_MAX
 #define PKV_ROW_HPW_MAX 8
@@ -17,7 +17,7 @@
 #define PKV_ROW_U 0
 #endif
 #ifndef PKV_ROW_R
-#define PKV_ROW_R 4
+#define PKV_ROW_R 3
 #endif
 
 namespace pkv {
@@ -44,7 +44,7 @@ int choose_hpw(int32_t dtype, int32_t head_dim, int32_t num_q_heads, int32_t num
 
 template <bool BF16, int D, int HPW, int G, bool PREFILL>
 hipError_t launch_one(const RowAttnArgs& a, hipStream_t stream) {
-  constexpr int U = PKV_ROW_U ? PKV_ROW_U : ((BF16 && G <= 2) ? 4 : 2);  // tokens per step
+  constexpr int U = PKV_ROW_U ? PKV_ROW_U : ((BF16 && G <= 4) ? 4 : 2);  // tokens per step
   const int n_hg = a.num_kv_heads / HPW;
   const int64_t rows = PREFILL ? (int64_t)a.max_rows : (int64_t)a.num_splits;
   const int64_t blocks = (int64_t)n_hg * a.num_seqs * rows;

@@ -274,9 +274,10 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
         }
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
+          // v_perm_b32: selector bytes 0-3 pick from the second operand, 4-7 from the first
           const uint32_t a0 = buf.v[u][w], a1 = buf.v[u + 1][w];
-          const uint32_t lo = (a0 & 0xffffu) | (a1 << 16);
-          const uint32_t hi = (a0 >> 16) | (a1 & 0xffff0000u);
+          const uint32_t lo = __builtin_amdgcn_perm(a1, a0, 0x05040100u);  // (a0.lo, a1.lo)
+          const uint32_t hi = __builtin_amdgcn_perm(a1, a0, 0x07060302u);  // (a0.hi, a1.hi)
 #pragma unroll
           for (int gq = 0; gq < G; ++gq) {
             o[gq][2 * w] = dot2_bf16(pp[gq], lo, o[gq][2 * w]);
