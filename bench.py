@@ -27,16 +27,18 @@ MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_traffic.md")
 
 
+DECODE_SOURCES = ("api.cpp", "common.hpp", "kernels.hpp", "row_attn.hip", "row_attn.hpp")
+
+
 def kernel_source_hash() -> str:
-    """sha256 over the HIP/C++ sources of libpkv.so (name + bytes, sorted)."""
+    """sha256 over the sources the decode split pass is built from (name + bytes, in order)."""
     import hashlib
 
     h = hashlib.sha256()
     d = os.path.join(ROOT, "paged_kv_gqa_mapping_amd", "csrc")
-    for name in sorted(os.listdir(d)):
-        if name.endswith((".hip", ".hpp", ".cpp", ".h")):
-            h.update(name.encode())
-            h.update(open(os.path.join(d, name), "rb").read())
+    for name in DECODE_SOURCES:
+        h.update(name.encode())
+        h.update(open(os.path.join(d, name), "rb").read())
     return h.hexdigest()
 
 

@@ -23,6 +23,12 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+// Column blocks of 32 (position, head) columns per wave (1 or 2); 2 reuses
+// every LDS operand fragment twice at one wave per SIMD.
+#ifndef PKV_PF_NBW
+#define PKV_PF_NBW 1
+#endif
+
 namespace pkv {
 
 namespace {
@@ -37,10 +43,11 @@ __device__ __forceinline__ int vt_column(int k) {
   return (k & ~15) + ((k16 & 7) >> 2) * 8 + (k16 >> 3) * 4 + (k16 & 3);
 }
 
-template <int D, int HW>
-__global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
-  constexpr int PB = 4 / HW;           // 32-position blocks per workgroup
-  constexpr int QP = 32 * PB;          // positions per workgroup
+template <int D, int HW, int NBW>
+__global__ __launch_bounds__(256, NBW == 1 ? 2 : 1) void prefill_mfma_kernel(PrefillArgs a) {
+  constexpr int PB = 4 / HW;           // position blocks (of 32 * NBW) per workgroup
+  constexpr int WP = 32 * NBW;         // positions per wave
+  constexpr int QP = WP * PB;          // positions per workgroup
   constexpr int KSTEPS = D / 16;       // contraction steps of Q K^T
   constexpr int MD = D / 32;           // 32-row blocks of O^T
   constexpr int KS = D + 8;            // LDS K row stride (elements): 16-byte pad
@@ -79,25 +86,33 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
   const int h = hg * HW + hl;
   const int g = (hg * HW) / G;
   const int shift = Lk - Lq;  // position of query i is shift + i
-  const int w_first = tile * QP + pb * 32;
-  const int w_last = min(w_first + 32, Lq) - 1;
+  const int w_first = tile * QP + pb * WP;
+  const int w_last = min(w_first + WP, Lq) - 1;
   const bool wave_active = w_first < Lq;
   const int w_min_pos = shift + w_first;
   const int w_max_pos = shift + w_last;
-  const int qi = w_first + col;
-  const bool col_valid = qi < Lq;
-  const int pos = col_valid ? shift + qi : Lk - 1;
+  // column block nb of the wave holds queries w_first + 32 nb + col
+  int pos[NBW];
+  bool col_valid[NBW];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) {
+    const int qi = w_first + 32 * nb + col;
+    col_valid[nb] = qi < Lq;
+    pos[nb] = col_valid[nb] ? shift + qi : Lk - 1;
+  }
   const int wg_max_pos = shift + min(tile * QP + QP, Lq) - 1;
   const int n_kt = wg_max_pos / kKT + 1;
 
   // Q^T as the B operand: lane (col, half) holds Q[col][16 kk + 8 half .. +8].
-  bf16x8_t qf[KSTEPS];
-  {
-    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)(q0 + qi) * Hq + h) * D + 8 * half;
+  bf16x8_t qf[NBW][KSTEPS];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) {
+    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)(q0 + w_first + 32 * nb + col) * Hq + h) * D + 8 * half;
+#pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
       uint4 x = make_uint4(0, 0, 0, 0);
-      if (col_valid) x = *reinterpret_cast<const uint4*>(qp + 16 * kk);
-      qf[kk] = __builtin_bit_cast(bf16x8_t, x);
+      if (col_valid[nb]) x = *reinterpret_cast<const uint4*>(qp + 16 * kk);
+      qf[nb][kk] = __builtin_bit_cast(bf16x8_t, x);
     }
   }
 
@@ -190,65 +205,94 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     }
   };
 
-  f32x16_t acc_o[MD];
-  for (int md = 0; md < MD; ++md)
-    for (int r = 0; r < 16; ++r) acc_o[md][r] = 0.f;
-  float m = kNegInf;  // running reference max of this lane's column (log2 units)
-  float lsum = 0.f;   // this half-wave's share of the column's weight sum
+  f32x16_t acc_o[NBW][MD];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_o[nb][md][r] = 0.f;
+  float m[NBW], lsum[NBW];  // running reference max (log2 units) and this half-wave's weight sum, per column
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) {
+    m[nb] = kNegInf;
+    lsum[nb] = 0.f;
+  }
   const float c = a.scale_log2;  // > 0
   const uint32_t kOnes = 0x3F803F80u;  // bf16 pair (1, 1)
 
   auto compute = [&](int buf, int key0) {
-    // S^T = K Q^T (raw scores)
-    f32x16_t acc_s[2];
-    for (int mb = 0; mb < 2; ++mb)
-      for (int r = 0; r < 16; ++r) acc_s[mb][r] = 0.f;
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8_t af = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const uint4*>(&lds_k[buf][(mb * 32 + col) * KS + 16 * kk + 8 * half]));
-        acc_s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[kk], acc_s[mb], 0, 0, 0);
-      }
-    }
-    // causal mask (only on tiles that reach past the wave's first position):
-    // key key0 + off(r) with off(r) = mb*32 + (r/4)*8 + half*4 + r%4 is
-    // visible iff off(r) - half*4 <= pos - key0 - half*4
-    if (key0 + kKT - 1 > w_min_pos) {
-      const int lim = pos - key0 - half * 4;
+    // S^T = K Q^T (raw scores); each K fragment feeds the NBW column blocks
+    f32x16_t acc_s[NBW][2];
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (mb * 32 + (r >> 2) * 8 + (r & 3) > lim) acc_s[mb][r] = kNegInf;
+        for (int r = 0; r < 16; ++r) acc_s[nb][mb][r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const bf16x8_t af = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const uint4*>(&lds_k[buf][(mb * 32 + col) * KS + 16 * kk + 8 * half]));
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+          acc_s[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[nb][kk], acc_s[nb][mb], 0, 0, 0);
+      }
     }
-    float mx = kNegInf;
-    for (int mb = 0; mb < 2; ++mb)
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc_s[mb][r]);
-    mx = halves_max(mx) * c;  // c > 0, so the max commutes with the scaling
-    if (wave_any(mx > m + kTau)) {
-      const float mn = fmaxf(m, mx);
-      const float alpha = exp2_hw(m - mn);
-      m = mn;
-      lsum *= alpha;
-      for (int md = 0; md < MD; ++md)
-        for (int r = 0; r < 16; ++r) acc_o[md][r] *= alpha;
+    uint32_t pw[NBW][16];
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+      // causal mask (only on tiles that reach past the block's first position):
+      // key key0 + off(r) with off(r) = mb*32 + (r/4)*8 + half*4 + r%4 is
+      // visible iff off(r) - half*4 <= pos - key0 - half*4
+      if (key0 + kKT - 1 > w_min_pos + 32 * nb) {
+        const int lim = pos[nb] - key0 - half * 4;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (mb * 32 + (r >> 2) * 8 + (r & 3) > lim) acc_s[nb][mb][r] = kNegInf;
+      }
+      float mx = kNegInf;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc_s[nb][mb][r]);
+      mx = halves_max(mx) * c;  // c > 0, so the max commutes with the scaling
+      if (wave_any(mx > m[nb] + kTau)) {
+        const float mn = fmaxf(m[nb], mx);
+        const float alpha = exp2_hw(m[nb] - mn);
+        m[nb] = mn;
+        lsum[nb] *= alpha;
+#pragma unroll
+        for (int md = 0; md < MD; ++md)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc_o[nb][md][r] *= alpha;
+      }
+      // P^T = 2^(c s - m), rounded to bf16, as the B operand of the four 16-key steps
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float s0 = acc_s[nb][i >> 3][(2 * i) & 15];
+        const float s1 = acc_s[nb][i >> 3][(2 * i + 1) & 15];
+        pw[nb][i] = pack_bf16x2(exp2_hw(fmaf(s0, c, -m[nb])), exp2_hw(fmaf(s1, c, -m[nb])));
+        lsum[nb] = dot2_bf16(pw[nb][i], kOnes, lsum[nb]);
+      }
     }
-    // P^T = 2^(c s - m), rounded to bf16, as the B operand of the four 16-key steps
-    uint32_t pw[16];
-    for (int i = 0; i < 16; ++i) {
-      const float s0 = acc_s[i >> 3][(2 * i) & 15];
-      const float s1 = acc_s[i >> 3][(2 * i + 1) & 15];
-      pw[i] = pack_bf16x2(exp2_hw(fmaf(s0, c, -m)), exp2_hw(fmaf(s1, c, -m)));
-      lsum = dot2_bf16(pw[i], kOnes, lsum);
-    }
-    // O^T += V^T P^T
+    // O^T += V^T P^T; each V^T fragment feeds the NBW column blocks
+#pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8_t bf =
-          __builtin_bit_cast(bf16x8_t, make_uint4(pw[4 * ks], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]));
+#pragma unroll
       for (int md = 0; md < MD; ++md) {
         const bf16x8_t af = __builtin_bit_cast(
             bf16x8_t, *reinterpret_cast<const uint4*>(&lds_v[buf][(md * 32 + col) * VS + 16 * ks + 8 * half]));
-        acc_o[md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc_o[md], 0, 0, 0);
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) {
+          const bf16x8_t bf = __builtin_bit_cast(
+              bf16x8_t, make_uint4(pw[nb][4 * ks], pw[nb][4 * ks + 1], pw[nb][4 * ks + 2], pw[nb][4 * ks + 3]));
+          acc_o[nb][md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc_o[nb][md], 0, 0, 0);
+        }
       }
     }
   };
@@ -288,16 +332,22 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
     __syncthreads();
   }
 
-  if (!wave_active || !col_valid) return;
-  const float inv = 1.0f / halves_sum(lsum);
-  uint16_t* op = (uint16_t*)a.out + ((int64_t)(q0 + qi) * Hq + h) * D + half * 4;
-  for (int md = 0; md < MD; ++md) {
-    for (int rr = 0; rr < 4; ++rr) {
-      const int r = rr * 4;
-      uint2 w;
-      w.x = pack_bf16x2(acc_o[md][r] * inv, acc_o[md][r + 1] * inv);
-      w.y = pack_bf16x2(acc_o[md][r + 2] * inv, acc_o[md][r + 3] * inv);
-      *reinterpret_cast<uint2*>(op + md * 32 + rr * 8) = w;
+  if (!wave_active) return;
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) {
+    if (!col_valid[nb]) continue;
+    const float inv = 1.0f / halves_sum(lsum[nb]);
+    uint16_t* op = (uint16_t*)a.out + ((int64_t)(q0 + w_first + 32 * nb + col) * Hq + h) * D + half * 4;
+#pragma unroll
+    for (int md = 0; md < MD; ++md) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int r = rr * 4;
+        uint2 w;
+        w.x = pack_bf16x2(acc_o[nb][md][r] * inv, acc_o[nb][md][r + 1] * inv);
+        w.y = pack_bf16x2(acc_o[nb][md][r + 2] * inv, acc_o[nb][md][r + 3] * inv);
+        *reinterpret_cast<uint2*>(op + md * 32 + rr * 8) = w;
+      }
     }
   }
 }
@@ -307,7 +357,8 @@ __global__ __launch_bounds__(256, 2) void prefill_mfma_kernel(PrefillArgs a) {
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int32_t head_dim, hipStream_t stream) {
   const int G = a.num_q_heads / a.num_kv_heads;
   const int HW = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
-  const int QP = 32 * (4 / HW);
+  constexpr int NBW = PKV_PF_NBW;
+  const int QP = 32 * NBW * (4 / HW);
   const int64_t n_qt = (a.max_seqlen_q + QP - 1) / QP;
   const int64_t blocks = n_qt * a.num_seqs * (a.num_q_heads / HW);
   if (blocks <= 0) return hipSuccess;
@@ -315,7 +366,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, int32_t head_dim, hipStream
   dim3 grid((unsigned)blocks), block(256);
 #define PKV_PREFILL_CASE(DD, HH)                                                              \
   if (head_dim == DD && HW == HH) {                                                           \
-    hipLaunchKernelGGL((prefill_mfma_kernel<DD, HH>), grid, block, 0, stream, a);             \
+    hipLaunchKernelGGL((prefill_mfma_kernel<DD, HH, NBW>), grid, block, 0, stream, a);        \
     return hipGetLastError();                                                                 \
   }
   PKV_PREFILL_CASE(128, 4)
