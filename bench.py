@@ -114,6 +114,8 @@ def main():
     ap.add_argument("--workload", type=int, default=5, help="workload number (5 = the mixed step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--graph", action="store_true",
+                    help="capture the step in a HIP graph and time graph replays (per-kernel events are not recorded)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -186,6 +188,26 @@ def main():
             rec(3)
         rec(4)
 
+    if args.graph:
+        # capture once (after a warm-up on the capture stream), then time replays
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            step()
+        torch.cuda.current_stream().wait_stream(cs)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        print(json.dumps({"workload": w.name, "graph_ms_per_step": round(ms, 5), "steps": args.steps}), flush=True)
+        return
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
