@@ -59,7 +59,8 @@ typedef enum {
   PKV_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent sizes */
   PKV_ERR_UNSUPPORTED = -2, /* valid but not built: head_dim, block size, group size, dtype */
   PKV_ERR_WORKSPACE = -3,   /* decode workspace missing or too small */
-  PKV_ERR_HIP = -4          /* the HIP runtime reported an error (text in pkv_last_error) */
+  PKV_ERR_HIP = -4,         /* the HIP runtime reported an error (text in pkv_last_error) */
+  PKV_ERR_OUT_OF_BLOCKS = -5 /* block manager: not enough free blocks (nothing was changed) */
 } pkv_status;
 
 /* Library version: major * 10000 + minor * 100 + patch. */
@@ -200,6 +201,67 @@ int pkv_paged_gather(const void* k_cache, const void* v_cache, const int32_t* bl
                      int32_t max_blocks_per_seq, const int32_t* cu_seqlens_k, int32_t num_seqs,
                      int32_t max_seqlen_k, void* k_out, void* v_out, int32_t num_kv_heads, int32_t head_dim,
                      int64_t num_blocks, int32_t block_size, int32_t dtype, void* stream);
+
+/*
+ * Block manager (host memory only; no device work).  Hands out the physical
+ * blocks of a paged KV cache and builds the block tables and slot mappings
+ * the calls above consume ("KV cache is divided into fixed-size blocks ...
+ * managed by a BlockManager: blocks are allocated on demand as sequences
+ * grow; prefix caching ... cached KV blocks are reused (reference-counted)",
+ * "Nano-vLLM Architecture and Performance", section "Paged KV Cache").
+ *
+ * - Blocks have reference counts.  A sequence's full prompt blocks are
+ *   looked up in a prefix cache keyed by a hash chained over the token ids of
+ *   all blocks up to and including that one; a hit is confirmed token by
+ *   token and shares the block (count + 1).  The first miss ends the lookup.
+ * - A full block written by one sequence only (count 1) is registered in the
+ *   cache; freed blocks (count 0) keep their registration and stay reusable
+ *   until the block is handed out again for new data (free blocks are reused
+ *   oldest first).  A sequence's partial last block is always its own.
+ * - Slots are int32: num_blocks * block_size must be below 2^31.
+ * - Each manager is internally locked; calls on one manager may come from
+ *   several threads.  Errors return a negative pkv_status with text in
+ *   pkv_bm_last_error() (thread-local); PKV_ERR_OUT_OF_BLOCKS leaves the
+ *   manager unchanged, so a caller can preempt and retry.
+ */
+typedef struct pkv_block_manager pkv_block_manager;
+
+/* A manager over num_blocks blocks of block_size tokens; NULL on error.
+ * enable_prefix_cache = 0 turns prefix reuse off. */
+pkv_block_manager* pkv_bm_create(int64_t num_blocks, int32_t block_size, int32_t enable_prefix_cache);
+void pkv_bm_destroy(pkv_block_manager* bm);
+const char* pkv_bm_last_error(void);
+
+int64_t pkv_bm_num_free_blocks(pkv_block_manager* bm);
+/* Reference count of a physical block (0 = free). */
+int32_t pkv_bm_block_refcount(pkv_block_manager* bm, int32_t block);
+
+/* 1 if a prompt of num_tokens token ids (host array) can be allocated now, 0 if not. */
+int pkv_bm_can_allocate(pkv_block_manager* bm, const int32_t* tokens, int64_t num_tokens);
+
+/* Allocate the blocks of a new sequence's prompt (tokens: host array of token
+ * ids), reusing cached prefix blocks.  *num_cached_tokens (may be NULL)
+ * receives how many leading tokens were found in the cache: their K/V are
+ * already stored, so only the rest need computing and storing. */
+int pkv_bm_allocate(pkv_block_manager* bm, int64_t seq_id, const int32_t* tokens, int64_t num_tokens,
+                    int64_t* num_cached_tokens);
+
+/* Append one token (decode); a new block is taken when the token starts one.
+ * *slot (may be NULL) receives the token's slot for pkv_kv_store. */
+int pkv_bm_append(pkv_block_manager* bm, int64_t seq_id, int32_t token, int32_t* slot);
+
+/* Release a sequence's blocks. */
+int pkv_bm_free(pkv_block_manager* bm, int64_t seq_id);
+
+/* Tokens of a sequence (its context length), or a negative status. */
+int64_t pkv_bm_seq_len(pkv_block_manager* bm, int64_t seq_id);
+
+/* Write the sequence's block table into out[0 .. capacity), padding unused
+ * entries with pad; returns the number of blocks or a negative status. */
+int32_t pkv_bm_block_table(pkv_block_manager* bm, int64_t seq_id, int32_t* out, int32_t capacity, int32_t pad);
+
+/* Slots of positions first_pos .. first_pos + count - 1 of a sequence. */
+int pkv_bm_slot_mapping(pkv_block_manager* bm, int64_t seq_id, int64_t first_pos, int64_t count, int32_t* out);
 
 #ifdef __cplusplus
 }

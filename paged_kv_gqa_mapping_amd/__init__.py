@@ -34,6 +34,8 @@ __all__ = [
     "lib",
     "library_path",
     "PkvError",
+    "OutOfBlocks",
+    "BlockManager",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -47,6 +49,10 @@ _lib = None
 
 class PkvError(RuntimeError):
     """A non-OK status from libpkv.so (message from pkv_last_error)."""
+
+
+class OutOfBlocks(PkvError):
+    """The block manager has too few free blocks (nothing was changed)."""
 
 
 def lib() -> ctypes.CDLL:
@@ -77,6 +83,29 @@ def lib() -> ctypes.CDLL:
     L.pkv_paged_prefill_attn.restype = ctypes.c_int
     L.pkv_paged_gather.argtypes = [P, P, P, I32, P, I32, I32, P, P, I32, I32, I64, I32, I32, V]
     L.pkv_paged_gather.restype = ctypes.c_int
+    L.pkv_bm_create.argtypes = [I64, I32, I32]
+    L.pkv_bm_create.restype = P
+    L.pkv_bm_destroy.argtypes = [P]
+    L.pkv_bm_destroy.restype = None
+    L.pkv_bm_last_error.restype = ctypes.c_char_p
+    L.pkv_bm_num_free_blocks.argtypes = [P]
+    L.pkv_bm_num_free_blocks.restype = I64
+    L.pkv_bm_block_refcount.argtypes = [P, I32]
+    L.pkv_bm_block_refcount.restype = I32
+    L.pkv_bm_can_allocate.argtypes = [P, P, I64]
+    L.pkv_bm_can_allocate.restype = ctypes.c_int
+    L.pkv_bm_allocate.argtypes = [P, I64, P, I64, ctypes.POINTER(I64)]
+    L.pkv_bm_allocate.restype = ctypes.c_int
+    L.pkv_bm_append.argtypes = [P, I64, I32, ctypes.POINTER(I32)]
+    L.pkv_bm_append.restype = ctypes.c_int
+    L.pkv_bm_free.argtypes = [P, I64]
+    L.pkv_bm_free.restype = ctypes.c_int
+    L.pkv_bm_seq_len.argtypes = [P, I64]
+    L.pkv_bm_seq_len.restype = I64
+    L.pkv_bm_block_table.argtypes = [P, I64, P, I32, I32]
+    L.pkv_bm_block_table.restype = I32
+    L.pkv_bm_slot_mapping.argtypes = [P, I64, I64, I64, P]
+    L.pkv_bm_slot_mapping.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -263,3 +292,86 @@ def paged_gather(k_cache, v_cache, block_tables, cu_seqlens_k, max_seqlen_k=None
         _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1], _ptr(cu_seqlens_k), B,
         int(max_seqlen_k), _ptr(k_out), _ptr(v_out), Hkv, D, NB, bs, _dtype_code(k_cache), _stream()))
     return k_out, v_out
+
+
+class BlockManager:
+    """Host-side block manager of libpkv.so (allocation, reference counts, prefix reuse).
+
+    ``tokens`` arguments are sequences of int token ids.  Methods raise
+    :class:`OutOfBlocks` when the pool is short (the manager is unchanged) and
+    :class:`PkvError` on bad arguments.
+    """
+
+    def __init__(self, num_blocks: int, block_size: int, prefix_cache: bool = True):
+        L = lib()
+        self._h = L.pkv_bm_create(int(num_blocks), int(block_size), 1 if prefix_cache else 0)
+        if not self._h:
+            raise PkvError(L.pkv_bm_last_error().decode())
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h and _lib is not None:
+            _lib.pkv_bm_destroy(h)
+
+    def _check(self, st):
+        if st < 0:
+            msg = lib().pkv_bm_last_error().decode()
+            raise (OutOfBlocks if st == -5 else PkvError)(msg)
+        return st
+
+    @staticmethod
+    def _arr(tokens):
+        import numpy as np
+
+        a = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        return a, (a.ctypes.data_as(ctypes.c_void_p) if a.size else None)
+
+    @property
+    def num_free_blocks(self) -> int:
+        return int(lib().pkv_bm_num_free_blocks(self._h))
+
+    def refcount(self, block: int) -> int:
+        return self._check(lib().pkv_bm_block_refcount(self._h, int(block)))
+
+    def can_allocate(self, tokens) -> bool:
+        a, p = self._arr(tokens)
+        return bool(self._check(lib().pkv_bm_can_allocate(self._h, p, a.size)))
+
+    def allocate(self, seq_id: int, tokens) -> int:
+        """Blocks for a new sequence's prompt; returns how many leading tokens were cached."""
+        a, p = self._arr(tokens)
+        cached = ctypes.c_int64(0)
+        self._check(lib().pkv_bm_allocate(self._h, int(seq_id), p, a.size, ctypes.byref(cached)))
+        return int(cached.value)
+
+    def append(self, seq_id: int, token: int) -> int:
+        """Append one token; returns its slot."""
+        slot = ctypes.c_int32(0)
+        self._check(lib().pkv_bm_append(self._h, int(seq_id), int(token), ctypes.byref(slot)))
+        return int(slot.value)
+
+    def free(self, seq_id: int) -> None:
+        self._check(lib().pkv_bm_free(self._h, int(seq_id)))
+
+    def seq_len(self, seq_id: int) -> int:
+        return int(self._check(lib().pkv_bm_seq_len(self._h, int(seq_id))))
+
+    def block_table(self, seq_id: int, width: int | None = None, pad: int = 0):
+        import numpy as np
+
+        n = -(-self.seq_len(seq_id) // self.block_size)
+        width = n if width is None else int(width)
+        out = np.empty(max(width, 0), dtype=np.int32)
+        p = out.ctypes.data_as(ctypes.c_void_p) if out.size else None
+        self._check(lib().pkv_bm_block_table(self._h, int(seq_id), p, width, int(pad)))
+        return out
+
+    def slot_mapping(self, seq_id: int, first_pos: int, count: int):
+        import numpy as np
+
+        out = np.empty(int(count), dtype=np.int32)
+        p = out.ctypes.data_as(ctypes.c_void_p) if out.size else None
+        self._check(lib().pkv_bm_slot_mapping(self._h, int(seq_id), int(first_pos), int(count), p))
+        return out

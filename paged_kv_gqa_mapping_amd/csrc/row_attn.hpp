@@ -166,7 +166,7 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
   // come from a 64-entry window of the table held one per lane and read with
   // readlane, so a lookup costs no memory round trip; the window moves when a
   // step leaves it.
-  int win0 = -1 << 30;  // first block index of the window
+  int win0 = -(1 << 30);  // first block index of the window
   int win = 0;          // this lane's entry: table[win0 + lane]
   auto step_row = [&](int t) -> int64_t {
     if (table) {
