@@ -179,3 +179,59 @@ def merge_states(states):
     num = sum(np.exp(m - M)[:, None] * o for m, _, o in states)
     den = sum(np.exp(m - M) * l for m, l, _ in states)
     return num / den[:, None]
+
+
+# ---------------------------------------------------------------- rotary embedding (next-row f2)
+#
+# The pages name a rotary position embedding layer that runs before the cache
+# write ("Nano-vLLM Architecture and Performance", project layout, and the
+# four-layer architecture page, layers/ listing) and a positions array that
+# the model runner prepares per token (same page, "ModelRunner"), but print no
+# formula.  The reading taken here is the rotary embedding as first published
+# (RoFormer): dimension pair j of a head turns by the angle
+# ``position * theta ** (-2 j / D)``, with the pair either (j, j + D/2)
+# ("rotate-half", the layout of the Qwen3 model the pages serve) or (2j, 2j+1)
+# ("interleaved").  theta is the caller's.
+
+
+def rope_pairs(D: int, interleaved: bool):
+    """Index arrays (first, second) of the D/2 rotated pairs of a head, pair j first."""
+    j = np.arange(D // 2)
+    if interleaved:
+        return 2 * j, 2 * j + 1
+    return j, j + D // 2
+
+
+def rope(x, positions, theta: float, interleaved: bool = False):
+    """Rotate every head of token ``i`` by its position.  x: float64 [N, H, D].
+
+    For pair j = (a, b) of a head, with angle t = positions[i] * theta**(-2j/D):
+    out[a] = x[a] cos t - x[b] sin t, out[b] = x[a] sin t + x[b] cos t
+    (multiplication of x[a] + i x[b] by e^{it}).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    N, H, D = x.shape
+    first, second = rope_pairs(D, interleaved)
+    inv_freq = float(theta) ** (-2.0 * np.arange(D // 2) / D)
+    angle = np.asarray(positions, dtype=np.float64)[:, None] * inv_freq[None, :]  # [N, D/2]
+    c = np.cos(angle)[:, None, :]
+    s = np.sin(angle)[:, None, :]
+    out = np.empty_like(x)
+    out[:, :, first] = x[:, :, first] * c - x[:, :, second] * s
+    out[:, :, second] = x[:, :, first] * s + x[:, :, second] * c
+    return out
+
+
+def rope_kv_store(q, k, v, positions, k_cache, v_cache, slot_mapping, block_size: int,
+                  theta: float, interleaved: bool, dtype: str):
+    """Rotary embedding of q and k followed by the cache write of the rotated k and of v.
+
+    Returns (q_rot, k_cache_out, v_cache_out): q_rot is float64 [N, Hq, D];
+    k_cache_out is the widened (float64) K cache with the rotated k rows at
+    their slots; v_cache_out holds the stored bits with v written as by
+    ``kv_store``.  Tokens with a negative slot are rotated in q only.
+    """
+    q_rot = rope(widen(q, dtype), positions, theta, interleaved)
+    k_rot = rope(widen(k, dtype), positions, theta, interleaved)
+    kc, vc = kv_store(widen(k_cache, dtype), v_cache, k_rot, v, slot_mapping, block_size)
+    return q_rot, kc, vc
