@@ -106,6 +106,33 @@ def cpu_baseline(w, kc, vc, budget_s: float = 12.0):
     }
 
 
+def measure_rope_kv_store(w, torch, pkv, dev, pq, dq, nk, nv, kc, vc, slots, bf, iters=20):
+    """Fused rotary embedding + cache write over the step's new tokens (chunk
+    tokens, then decode tokens, at their own positions), timed on its own after
+    the step: a 512 MiB read between launches evicts the inputs from the caches."""
+    q = torch.cat([pq, dq], dim=0).contiguous()
+    pos = dev(w.store_positions)
+    N, Hq, D = q.shape
+    elt = 2 if bf else 4
+    algo = 2 * N * (Hq + 2 * w.num_kv_heads) * D * elt + 8 * N
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    ts = []
+    for i in range(iters + 2):
+        flush.sum()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        pkv.rope_kv_store(q, nk, nv, pos, kc, vc, slots, 1e6, False)
+        b.record()
+        torch.cuda.synchronize()
+        if i >= 2:
+            ts.append(a.elapsed_time(b))
+    ms = sum(ts) / len(ts)
+    gbs = algo / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 5), "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+            "tokens": int(N), "algorithmic_bytes": int(algo), "rope_theta": 1e6,
+            "note": "next-row kernel, timed separately after the step (not part of value)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -114,6 +141,7 @@ def main():
     ap.add_argument("--workload", type=int, default=5, help="workload number (5 = the mixed step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--no-rope", action="store_true", help="skip the separate fused rope + kv_store measurement")
     ap.add_argument("--graph", action="store_true",
                     help="capture the step in a HIP graph and time graph replays (per-kernel events are not recorded)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -254,6 +282,9 @@ def main():
         roofline = {"bound": "mfma", "achieved": round(kernels["prefill"]["TFLOP/s"], 2), "peak": MFMA_BF16_PEAK_TFS,
                     "unit": "TFLOP/s", "frac": kernels["prefill"]["frac_mfma"], "traffic": None,
                     "kernel": "prefill_mfma_kernel"}
+
+    if has_dec and has_pre and not args.no_rope:
+        kernels["rope_kv_store"] = measure_rope_kv_store(w, torch, pkv, dev, pq, dq, nk, nv, kc, vc, slots, bf)
 
     cpu = None
     if not args.no_cpu_baseline and has_dec:

@@ -94,6 +94,39 @@ int pkv_kv_store(const void* k, const void* v, void* k_cache, void* v_cache, con
                  int32_t block_size, int32_t dtype, void* stream);
 
 /*
+ * rope_kv_store -- rotary position embedding of q and k, fused with the cache
+ * write of the rotated k and of v.  The pages list a rotary embedding layer
+ * that runs before attention ("Nano-vLLM Architecture and Performance",
+ * project layout, layers/rotary_embedding.py) and a per-token positions
+ * array built by the model runner (same page, section "How It Works
+ * End-to-End"); they print no formula.  The rotation is the RoFormer one:
+ * pair j of every head of token i turns by the angle
+ * positions[i] * rope_theta^(-2j / head_dim), i.e. (x, y) becomes
+ * (x cos t - y sin t, x sin t + y cos t).
+ *
+ *   q             [num_tokens, num_q_heads, head_dim], rotated IN PLACE.
+ *   k, v          [num_tokens, num_kv_heads, head_dim], read only.
+ *   positions     [num_tokens] int32, the token's position in its sequence.
+ *   k_cache,
+ *   v_cache       [num_blocks, block_size, num_kv_heads, head_dim]; the rotated
+ *                 k row and the v row of token i are written at slot
+ *                 slot_mapping[i], exactly where pkv_kv_store puts them.  A
+ *                 negative slot skips the cache write (q is still rotated).
+ *   rope_theta    > 1, the base of the pair frequencies (model constant).
+ *   interleaved   0: pair j is (j, j + head_dim/2) ("rotate-half");
+ *                 1: pair j is (2j, 2j + 1).
+ *
+ * Arithmetic: angles are reduced modulo 2 pi in fp64, (cos, sin) and the
+ * products are fp32, results rounded to nearest even to the storage dtype,
+ * so each output is within one unit in the last place of the exact rotation.
+ * v moves bit-exact.  Same preconditions on slots as pkv_kv_store.
+ */
+int pkv_rope_kv_store(void* q, const void* k, const void* v, const int32_t* positions, void* k_cache, void* v_cache,
+                      const int32_t* slot_mapping, int64_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int64_t num_blocks, int32_t block_size, double rope_theta,
+                      int32_t interleaved, int32_t dtype, void* stream);
+
+/*
  * Decode attention, split-K.  Sequence b's single query q[b] attends all
  * context_lens[b] tokens of its context (the token just stored included),
  * read through row b of block_tables: out = softmax(scale * q K^T) V per

@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
     L.pkv_last_error.restype = ctypes.c_char_p
     L.pkv_kv_store.argtypes = [P, P, P, P, P, I64, I32, I32, I64, I32, I32, V]
     L.pkv_kv_store.restype = ctypes.c_int
+    L.pkv_rope_kv_store.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, I32, I64, I32, ctypes.c_double, I32, I32, V]
+    L.pkv_rope_kv_store.restype = ctypes.c_int
     L.pkv_decode_split_tokens.argtypes = [I32, I32, I32, I32, I32, I32, I32]
     L.pkv_decode_split_tokens.restype = I32
     L.pkv_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
@@ -168,6 +170,28 @@ def kv_store(k, v, k_cache, v_cache, slot_mapping) -> None:
         raise ValueError("shape mismatch among k, v, k_cache, v_cache, slot_mapping")
     _check(lib().pkv_kv_store(_ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), N, Hkv, D, NB, bs,
                               _dtype_code(k), _stream()))
+
+
+def rope_kv_store(q, k, v, positions, k_cache, v_cache, slot_mapping, rope_theta, interleaved=False) -> None:
+    """Rotary embedding of q (in place, [N, Hq, D]) and k, then the cache write of the
+    rotated k and of v at slot_mapping[i] (negative: no cache write)."""
+    torch = _torch()
+    _dev(q, "q", ndim=3)
+    _dev(k, "k", q.dtype, 3)
+    _dev(v, "v", q.dtype, 3)
+    _dev(positions, "positions", torch.int32, 1)
+    _dev(k_cache, "k_cache", q.dtype, 4)
+    _dev(v_cache, "v_cache", q.dtype, 4)
+    _dev(slot_mapping, "slot_mapping", torch.int32, 1)
+    N, Hq, D = q.shape
+    _, Hkv, _ = k.shape
+    NB, bs, Hkv2, D2 = k_cache.shape
+    if (k.shape != (N, Hkv, D) or v.shape != k.shape or v_cache.shape != k_cache.shape or (Hkv2, D2) != (Hkv, D)
+            or positions.shape[0] != N or slot_mapping.shape[0] != N):
+        raise ValueError("shape mismatch among q, k, v, positions, k_cache, v_cache, slot_mapping")
+    _check(lib().pkv_rope_kv_store(_ptr(q), _ptr(k), _ptr(v), _ptr(positions), _ptr(k_cache), _ptr(v_cache),
+                                   _ptr(slot_mapping), N, Hq, Hkv, D, NB, bs, float(rope_theta), int(bool(interleaved)),
+                                   _dtype_code(q), _stream()))
 
 
 def decode_split_tokens(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, block_size, dtype_code):

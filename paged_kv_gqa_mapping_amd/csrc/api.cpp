@@ -192,6 +192,40 @@ int pkv_kv_store(const void* k, const void* v, void* k_cache, void* v_cache, con
                     "kv_store launch");
 }
 
+int pkv_rope_kv_store(void* q, const void* k, const void* v, const int32_t* positions, void* k_cache, void* v_cache,
+                      const int32_t* slot_mapping, int64_t num_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int64_t num_blocks, int32_t block_size, double rope_theta,
+                      int32_t interleaved, int32_t dtype, void* stream) {
+  if (num_tokens < 0) return fail(PKV_ERR_INVALID_ARG, "num_tokens %lld < 0", (long long)num_tokens);
+  int st = check_cache_shape(num_kv_heads, head_dim, num_blocks, block_size, dtype, true);
+  if (st) return st;
+  if (num_q_heads < 1 || num_q_heads > 1024)
+    return fail(PKV_ERR_INVALID_ARG, "num_q_heads %d outside [1, 1024]", num_q_heads);
+  if (!(rope_theta > 1.0) || !std::isfinite(rope_theta))
+    return fail(PKV_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
+  if (interleaved != 0 && interleaved != 1) return fail(PKV_ERR_INVALID_ARG, "interleaved %d is not 0 or 1", interleaved);
+  if (num_tokens == 0) return PKV_OK;
+  if (!q || !k || !v || !positions || !k_cache || !v_cache || !slot_mapping)
+    return fail(PKV_ERR_INVALID_ARG, "null pointer among q, k, v, positions, k_cache, v_cache, slot_mapping");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PKV_ERR_INVALID_ARG, "q, k, v, k_cache and v_cache must be 16-byte aligned");
+  if (num_tokens > 0x7fffffffLL) return fail(PKV_ERR_UNSUPPORTED, "num_tokens %lld too large", (long long)num_tokens);
+  pkv::RopeStoreArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.positions = positions;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.log2_theta = std::log2(rope_theta);
+  return hip_status(pkv::launch_rope_kv_store(a, dtype, head_dim, interleaved != 0, static_cast<hipStream_t>(stream)),
+                    "rope_kv_store launch");
+}
+
 int32_t pkv_decode_split_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                 int32_t max_context_len, int32_t block_size, int32_t dtype) {
   (void)num_q_heads;

@@ -65,6 +65,24 @@ struct PrefillArgs {
 // bf16 matrix-core prefill.
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int32_t head_dim, hipStream_t stream);
 
+// Arguments of the fused rotary embedding + cache write.
+struct RopeStoreArgs {
+  void* q;                       // [num_tokens, num_q_heads, D], rotated in place
+  const void* k;                 // [num_tokens, num_kv_heads, D]
+  const void* v;                 // [num_tokens, num_kv_heads, D]
+  const int32_t* positions;      // [num_tokens]
+  void* k_cache;                 // [num_blocks * block_size, num_kv_heads, D]
+  void* v_cache;
+  const int32_t* slot_mapping;   // [num_tokens], negative = no cache write
+  int64_t num_tokens;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  double log2_theta;             // pair j turns by position * 2^(-2j/D * log2_theta)
+};
+
+hipError_t launch_rope_kv_store(const RopeStoreArgs& a, int32_t dtype, int32_t head_dim, bool interleaved,
+                                hipStream_t stream);
+
 // Row-attention instantiation exists for this shape?
 bool row_attn_supported(int32_t dtype, int32_t head_dim, int32_t num_q_heads, int32_t num_kv_heads);
 

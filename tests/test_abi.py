@@ -98,3 +98,27 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(pkv, "_lib", None)
     with pytest.raises(pkv.PkvError):
         pkv.lib()
+
+
+@needs_lib
+def test_rope_kv_store_argument_errors_before_launch():
+    L = pkv.lib()
+    p = 1 << 20
+
+    def call(**kw):
+        a = dict(q=p, k=p, v=p, pos=p, kc=p, vc=p, sl=p, N=4, Hq=32, Hkv=8, D=128, NB=10, bs=16, theta=1e6,
+                 inter=0, dtype=1)
+        a.update(kw)
+        return L.pkv_rope_kv_store(a["q"], a["k"], a["v"], a["pos"], a["kc"], a["vc"], a["sl"], a["N"], a["Hq"],
+                                   a["Hkv"], a["D"], a["NB"], a["bs"], a["theta"], a["inter"], a["dtype"], None)
+    assert call(D=96) == -2
+    assert call(bs=48) == -2
+    assert call(dtype=7) == -2
+    assert call(N=-1) == -1
+    assert call(Hq=0) == -1
+    assert call(theta=0.5) == -1
+    assert call(theta=float("nan")) == -1
+    assert call(inter=2) == -1
+    assert call(q=None) == -1
+    assert call(k=p + 8) == -1           # misaligned
+    assert call(N=0, q=None) == 0         # nothing to do: no launch, no pointer needed

@@ -189,6 +189,8 @@ class Workload:
     new_k: np.ndarray
     new_v: np.ndarray
     slot_mapping: np.ndarray
+    # position in its sequence of each appended token (same order as slot_mapping)
+    store_positions: np.ndarray | None = None
     # decode part
     dec_q: np.ndarray | None = None
     dec_block_tables: np.ndarray | None = None
@@ -338,11 +340,12 @@ def build(
         return t
 
     # slot mapping of the appended tokens: prefill tokens first, then decode tokens
-    slots = []
+    slots, positions = [], []
     for i in pre + dec:
         s, ids = seqs[i], seq_blocks[i]
         for p in range(s.total - s.new, s.total):
             slots.append(ids[p // bs] * bs + p % bs)
+            positions.append(p)
     slot_mapping = np.asarray(slots, dtype=np.int32)
 
     hkv, d = num_kv_heads, head_dim
@@ -381,7 +384,7 @@ def build(
         scale=(1.0 / math.sqrt(d)) if scale is None else float(scale),
         poison_block=int(poison_block), refcount=pool.refcount.copy(), shared_blocks=list(shared_ids),
         k_cache=k_cache, v_cache=v_cache, new_k=new_k, new_v=new_v, slot_mapping=slot_mapping,
-        seqs=list(seqs),
+        store_positions=np.asarray(positions, dtype=np.int32), seqs=list(seqs),
     )
     if pre:
         w.pre_q = q_all[:n_pre_q]
