@@ -133,6 +133,27 @@ def measure_rope_kv_store(w, torch, pkv, dev, pq, dq, nk, nv, kc, vc, slots, bf,
             "note": "next-row kernel, timed separately after the step (not part of value)"}
 
 
+def measure_cascade(w, torch, cascade_decode, out, plain_ms, iters=20):
+    """Shared-prefix decode of the step's decode batch (group pass, split pass and
+    merge), timed on its own after the step, against the step's plain decode."""
+    for _ in range(3):
+        cascade_decode(out)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for a, b in ev:
+        a.record()
+        cascade_decode(out)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b) for a, b in ev) / iters
+    logical, unique = w.decode_kv_bytes(), w.decode_kv_bytes_unique()
+    return {"ms": round(ms, 5), "plain_decode_ms": round(plain_ms, 5),
+            "logical_GB/s": round(logical / (ms * 1e-3) / 1e9, 1),
+            "unique_GB/s": round(unique / (ms * 1e-3) / 1e9, 1),
+            "frac_hbm_unique": round(unique / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "unique_kv_gb": round(unique / 1e9, 4),
+            "note": "next-row path (group pass + split pass + merge), timed separately after the step"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,7 +162,10 @@ def main():
     ap.add_argument("--workload", type=int, default=5, help="workload number (5 = the mixed step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--split-tokens", type=int, default=0)
-    ap.add_argument("--no-rope", action="store_true", help="skip the separate fused rope + kv_store measurement")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the separately timed next-row measurements (fused rope + kv_store, cascade decode)")
+    ap.add_argument("--cascade", action="store_true",
+                    help="decode with shared-prefix (cascade) decode inside the step instead of plain split-K decode")
     ap.add_argument("--graph", action="store_true",
                     help="capture the step in a HIP graph and time graph replays (per-kernel events are not recorded)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -188,6 +212,21 @@ def main():
                                                              w.block_size, 1 if bf else 0)
         ws_bytes = pkv.decode_workspace_bytes(B, Hq, D, w.max_context_len, split)
         ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+        shared, goff, gseq, gmax, smax, gown = w.cascade_groups()
+        has_groups = len(goff) > 1
+        if has_groups:
+            csh, cgo, cgs = dev(shared), dev(goff), dev(gseq)
+            cws = torch.empty(max(pkv.cascade_workspace_bytes(B, Hq, w.num_kv_heads, D, w.max_context_len, gown, 0,
+                                                              len(goff) - 1, gmax, smax), 16),
+                              dtype=torch.uint8, device="cuda")
+            cout = torch.empty_like(dq)
+        if args.cascade and not has_groups:
+            print("--cascade needs a workload with shared prefixes", file=sys.stderr)
+            sys.exit(2)
+
+        def cascade_decode(o):
+            pkv.cascade_decode_attn(dq, kc, vc, dbt, dcl, csh, cgo, cgs, w.scale, o, max_context_len=w.max_context_len,
+                                    max_group_size=gmax, max_shared_len=smax, max_own_len=gown, workspace=cws)
     if has_pre:
         pq, pbt, cuq, cuk = dev(w.pre_q, bf), dev(w.pre_block_tables), dev(w.cu_seqlens_q), dev(w.cu_seqlens_k)
         pout = torch.empty_like(pq)
@@ -206,7 +245,10 @@ def main():
             pkv.paged_prefill_attn(pq, kc, vc, cuq, cuk, pbt, pout, max_seqlen_q=w.max_seqlen_q,
                                    max_seqlen_k=w.max_seqlen_k, scale=w.scale)
         rec(2)
-        if has_dec:
+        if has_dec and args.cascade:
+            cascade_decode(dout)
+            rec(3)
+        elif has_dec:
             pkv.paged_decode_split(dq, kc, vc, dbt, dcl, w.scale, dout, max_context_len=w.max_context_len,
                                    split_tokens=split, workspace=ws)
             rec(3)
@@ -256,14 +298,16 @@ def main():
     dec_io = w.decode_io_bytes()
     flops = w.prefill_flops()
     store_bytes = w.store_bytes()
-    split_bytes = kv_bytes + dec_io
+    # with --cascade the timed decode is the whole shared-prefix call, which reads the unique bytes
+    split_bytes = (w.decode_kv_bytes_unique() if args.cascade else kv_bytes) + dec_io
     achieved_gbs = split_bytes / (t_split * 1e-3) / 1e9 if has_dec else 0.0
 
     kernels = {
         "kv_store": {"ms": round(t_store, 5), "GB/s": round(store_bytes / (t_store * 1e-3) / 1e9, 1),
                      "tokens": int(len(w.slot_mapping))},
         "decode_split": {"ms": round(t_split, 5), "GB/s": round(achieved_gbs, 1),
-                         "frac_hbm": round(achieved_gbs / HBM_PEAK_GBS, 4), "split_tokens": int(split) if has_dec else 0},
+                         "frac_hbm": round(achieved_gbs / HBM_PEAK_GBS, 4),
+                         "split_tokens": (None if args.cascade else int(split)) if has_dec else 0},
         "decode_reduce": {"ms": round(t_red, 5)},
     }
     if has_pre:
@@ -272,10 +316,11 @@ def main():
                               "frac_mfma": round(tfs / MFMA_BF16_PEAK_TFS, 4), "tflop": round(flops / 1e12, 5)}
     if has_dec:
         value = kv_bytes / (ms_per_step * 1e-3) / 1e9
-        traffic = measured_traffic() if args.workload == 5 and not args.split_tokens else None
+        traffic = measured_traffic() if args.workload == 5 and not args.split_tokens and not args.cascade else None
         roofline = {"bound": "hbm", "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                    "kernel": "row_attn_kernel (decode split pass)",
+                    "kernel": ("shared-prefix decode call (group pass + split pass + merge)" if args.cascade
+                               else "row_attn_kernel (decode split pass)"),
                     "algorithmic_bytes_per_launch": int(split_bytes)}
     else:
         value = flops / (ms_per_step * 1e-3) / 1e12
@@ -283,7 +328,9 @@ def main():
                     "unit": "TFLOP/s", "frac": kernels["prefill"]["frac_mfma"], "traffic": None,
                     "kernel": "prefill_mfma_kernel"}
 
-    if has_dec and has_pre and not args.no_rope:
+    if has_dec and has_groups and not args.cascade and not args.no_extras:
+        kernels["cascade_decode"] = measure_cascade(w, torch, cascade_decode, cout, t_split + t_red)
+    if has_dec and has_pre and not args.no_extras:
         kernels["rope_kv_store"] = measure_rope_kv_store(w, torch, pkv, dev, pq, dq, nk, nv, kc, vc, slots, bf)
 
     cpu = None

@@ -188,6 +188,56 @@ int pkv_paged_decode_reduce(const void* q, const void* k_cache, const void* v_ca
                             int32_t split_tokens, void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * Shared-prefix ("cascade") decode: the same result as pkv_paged_decode_attn
+ * (up to rounding), for a batch in which groups of sequences begin with the
+ * same cached blocks (prefix caching: blocks of a common prefix are reused
+ * with reference counts, "Nano-vLLM Architecture and Performance", section
+ * "Key Features", item "Paged KV Cache"; the nano-vllm README's feature list
+ * names the sharing of KV blocks for common prefixes).  The shared keys
+ * are read once per group instead of once per member: a group pass on the
+ * matrix cores attends every member's query to the shared blocks, chunk by
+ * chunk, and the split pass attends each sequence's own keys; the reduction
+ * merges both kinds of softmax state with the split-K formula.
+ *
+ * Arguments as pkv_paged_decode_attn, plus:
+ *   shared_lens    [num_seqs] int32: keys of sequence b that lie in its
+ *                  group's shared blocks (a multiple of block_size, below
+ *                  context_lens[b]); 0 for a sequence in no group.
+ *   group_offsets  [num_groups + 1] int32, non-decreasing from 0: group gi is
+ *                  group_seqs[group_offsets[gi] .. group_offsets[gi + 1]).
+ *   group_seqs     sequence indices; every sequence with shared_lens > 0 is
+ *                  in exactly one group; members of a group have the same
+ *                  shared_lens and the same first shared_lens / block_size
+ *                  block ids.
+ *   max_group_size >= the largest group; max_shared_len >= every shared_lens
+ *                  entry, a multiple of block_size below max_context_len.
+ *   max_own_len    >= every context_lens[b] - shared_lens[b] (the keys a
+ *                  sequence attends on its own); it sizes the split pass.
+ *                  0 means max_context_len.
+ *   split_tokens   split length of the split pass, or 0 for the library's
+ *                  choice for max_own_len.
+ *   workspace      at least pkv_cascade_workspace_bytes(...) bytes (same
+ *                  sizes and split_tokens as the call).
+ * With num_groups == 0 or max_shared_len == 0 this is pkv_paged_decode_attn
+ * (shared_lens, group_offsets and group_seqs are not read).  The group pass
+ * needs dtype PKV_BF16 (PKV_ERR_UNSUPPORTED otherwise).  The device-side
+ * preconditions above are not checked.
+ */
+int pkv_cascade_decode_attn(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
+                            const int32_t* shared_lens, const int32_t* group_offsets, const int32_t* group_seqs,
+                            int32_t num_groups, int32_t max_group_size, int32_t max_shared_len, int32_t max_own_len,
+                            float scale, void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int64_t num_blocks, int32_t block_size, int32_t dtype,
+                            int32_t split_tokens, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes pkv_cascade_decode_attn needs for these sizes and split_tokens
+ * (0 when it writes every output directly). */
+int64_t pkv_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t max_context_len, int32_t max_own_len, int32_t split_tokens,
+                                    int32_t num_groups, int32_t max_group_size, int32_t max_shared_len);
+
+/*
  * Causal varlen prefill attention (chunked prefill and cached prefixes).
  * Sequence b has Lq = cu_seqlens_q[b+1] - cu_seqlens_q[b] new queries and
  * Lk = cu_seqlens_k[b+1] - cu_seqlens_k[b] keys in all, Lq <= Lk.  Query i

@@ -72,6 +72,11 @@ def lib() -> ctypes.CDLL:
     L.pkv_kv_store.restype = ctypes.c_int
     L.pkv_rope_kv_store.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, I32, I64, I32, ctypes.c_double, I32, I32, V]
     L.pkv_rope_kv_store.restype = ctypes.c_int
+    L.pkv_cascade_decode_attn.argtypes = [P, P, P, P, I32, P, I32, P, P, P, I32, I32, I32, I32, F, P, I32, I32, I32,
+                                          I32, I64, I32, I32, I32, P, I64, V]
+    L.pkv_cascade_decode_attn.restype = ctypes.c_int
+    L.pkv_cascade_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32, I32, I32]
+    L.pkv_cascade_workspace_bytes.restype = I64
     L.pkv_decode_split_tokens.argtypes = [I32, I32, I32, I32, I32, I32, I32]
     L.pkv_decode_split_tokens.restype = I32
     L.pkv_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
@@ -252,6 +257,55 @@ def paged_decode_reduce(q, k_cache, v_cache, block_tables, context_lens, scale, 
     """Second pass of paged_decode_attn (merge of the split states); same arguments and workspace as the first."""
     return _decode("pkv_paged_decode_reduce", q, k_cache, v_cache, block_tables, context_lens, scale, out,
                    max_context_len, split_tokens, workspace)
+
+
+def cascade_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, max_own_len,
+                            split_tokens, num_groups, max_group_size, max_shared_len) -> int:
+    return int(lib().pkv_cascade_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                                                 max_own_len, split_tokens, num_groups, max_group_size,
+                                                 max_shared_len))
+
+
+def cascade_decode_attn(q, k_cache, v_cache, block_tables, context_lens, shared_lens, group_offsets, group_seqs,
+                        scale, out, max_context_len=None, max_group_size=None, max_shared_len=None, max_own_len=None,
+                        split_tokens=0, workspace=None):
+    """Shared-prefix decode: as paged_decode_attn, with groups of sequences whose first
+    shared_lens[b] keys are the same blocks attended once per group.  Sizes left as None
+    are read back from the device tensors (a synchronisation)."""
+    torch = _torch()
+    _dev(q, "q", ndim=3)
+    _dev(k_cache, "k_cache", q.dtype, 4)
+    _dev(v_cache, "v_cache", q.dtype, 4)
+    for t, n in ((block_tables, "block_tables"), (context_lens, "context_lens"), (shared_lens, "shared_lens"),
+                 (group_offsets, "group_offsets"), (group_seqs, "group_seqs")):
+        _dev(t, n, torch.int32)
+    _dev(out, "out", q.dtype, 3)
+    B, Hq, D = q.shape
+    NB, bs, Hkv, D2 = k_cache.shape
+    if out.shape != q.shape or D2 != D or v_cache.shape != k_cache.shape or block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("shape mismatch among q, k_cache, v_cache, block_tables")
+    if context_lens.shape[0] != B or shared_lens.shape[0] != B:
+        raise ValueError("context_lens and shared_lens need one entry per sequence")
+    num_groups = group_offsets.shape[0] - 1
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if B else 0
+    if max_shared_len is None:
+        max_shared_len = int(shared_lens.max().item()) if B else 0
+    if max_group_size is None:
+        max_group_size = int((group_offsets[1:] - group_offsets[:-1]).max().item()) if num_groups > 0 else 0
+    if max_own_len is None:
+        max_own_len = int((context_lens - shared_lens).max().item()) if B else 0
+    split = int(split_tokens)
+    need = cascade_workspace_bytes(B, Hq, Hkv, D, max_context_len, max_own_len, split, num_groups, max_group_size,
+                                   max_shared_len)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check(lib().pkv_cascade_decode_attn(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        max_context_len, _ptr(shared_lens), _ptr(group_offsets), _ptr(group_seqs), num_groups, max_group_size,
+        max_shared_len, max_own_len, float(scale), _ptr(out), B, Hq, Hkv, D, NB, bs, _dtype_code(q), split,
+        _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream()))
 
 
 def paged_prefill_attn(q, k, v, cu_seqlens_q, cu_seqlens_k, block_tables, out, max_seqlen_q=None,

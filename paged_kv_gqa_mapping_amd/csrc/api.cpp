@@ -91,11 +91,60 @@ struct DecodeCall {
   bool empty;
 };
 
+// Launch plan of a decode call: split length and count, and for shared-prefix
+// decode the group pass's chunk length and count (prefix states per pair).
+struct DecodePlan {
+  int32_t split = 0;
+  int32_t S = 1;      // split states per pair (grid splits)
+  int32_t chunk = 0;  // keys per group-pass state
+  int32_t C = 0;      // group-pass states per pair
+};
+
+// Shared-prefix plan.  The split pass only covers each sequence's own keys,
+// so its split comes from the longest of those (max_own_len).  The group pass
+// takes chunks of at least 256 keys (4 tiles), doubled while its grid would
+// need more than one round of 512 workgroups (2 per CU): a longer chunk then
+// costs no time in that pass and halves the states the merge reads.
+DecodePlan cascade_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_context_len,
+                        int32_t max_own_len, int32_t split_tokens, int32_t num_groups, int32_t max_group_size,
+                        int32_t max_shared_len) {
+  DecodePlan p;
+  const int32_t own = (max_own_len > 0 && max_own_len < max_context_len) ? max_own_len : max_context_len;
+  p.split = split_tokens;
+  if (!p.split) {
+    // Own keys are often few (a short suffix behind a long shared prompt), and the
+    // plain rule's 256/512-token floor would then leave a small grid of long
+    // waves; splits down to 64 keys keep about 2048 waves in flight.  Long own
+    // keys keep the plain rule.
+    const int64_t base = (int64_t)std::max(num_seqs, 1) * std::max(1, num_kv_heads / 8);
+    int32_t fine = 64;
+    while (fine < own && base * ((own + fine - 1) / fine) > 2048) fine *= 2;
+    p.split = std::min(fine, auto_split(std::max(num_seqs, 1), std::max(num_kv_heads, 1), own));
+  }
+  p.S = std::max(1, (own + p.split - 1) / p.split);
+  if (num_groups > 0 && max_shared_len > 0) {
+    const int64_t wgs = pkv::shared_prefix_wgs_per_chunk(num_q_heads, num_kv_heads, num_groups, max_group_size);
+    p.chunk = 256;
+    while (p.chunk < max_shared_len && wgs * ((max_shared_len + p.chunk - 1) / p.chunk) > 512) p.chunk *= 2;
+    p.C = (max_shared_len + p.chunk - 1) / p.chunk;
+  }
+  return p;
+}
+
+// Workspace of S split states plus C prefix states per (sequence, query head); none when a
+// single state per pair is written straight to the output.
+int64_t state_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int64_t S, int64_t C) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || S <= 0) return 0;
+  if (S + C <= 1) return 0;
+  return (int64_t)num_seqs * num_q_heads * (S + C) * (head_dim + 2) * (int64_t)sizeof(float);
+}
+
 int prepare_decode(DecodeCall& call, const void* q, const void* k_cache, const void* v_cache,
                    const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                    int32_t max_context_len, float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
                    int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, int32_t block_size, int32_t dtype,
-                   int32_t split_tokens, void* workspace, int64_t workspace_bytes) {
+                   int32_t split_tokens, void* workspace, int64_t workspace_bytes,
+                   const DecodePlan* plan = nullptr) {
   call.empty = false;
   if (num_seqs < 0) return fail(PKV_ERR_INVALID_ARG, "num_seqs %d < 0", num_seqs);
   int st = check_cache_shape(num_kv_heads, head_dim, num_blocks, block_size, dtype, true);
@@ -117,9 +166,11 @@ int prepare_decode(DecodeCall& call, const void* q, const void* k_cache, const v
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
   if (split_tokens < 0 || split_tokens % 64)
     return fail(PKV_ERR_INVALID_ARG, "split_tokens %d is not 0 or a positive multiple of 64", split_tokens);
-  const int32_t split = split_tokens ? split_tokens : auto_split(num_seqs, num_kv_heads, max_context_len);
-  const int32_t S = std::max(1, (max_context_len + split - 1) / split);
-  const int64_t need = pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, split);
+  const int32_t split =
+      plan ? plan->split : split_tokens ? split_tokens : auto_split(num_seqs, num_kv_heads, max_context_len);
+  const int32_t S = plan ? plan->S : std::max(1, (max_context_len + split - 1) / split);
+  const int32_t prefix_states = plan ? plan->C : 0;
+  const int64_t need = state_bytes(num_seqs, num_q_heads, head_dim, S, prefix_states);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PKV_ERR_WORKSPACE, "decode workspace of %lld bytes needed, %lld given%s", (long long)need,
                 (long long)workspace_bytes, workspace ? "" : " (NULL)");
@@ -137,7 +188,7 @@ int prepare_decode(DecodeCall& call, const void* q, const void* k_cache, const v
   a.context_lens = context_lens;
   a.out = out;
   a.ws_o = need > 0 ? static_cast<float*>(workspace) : nullptr;
-  a.ws_ml = need > 0 ? a.ws_o + (int64_t)num_seqs * num_q_heads * S * head_dim : nullptr;
+  a.ws_ml = need > 0 ? a.ws_o + (int64_t)num_seqs * num_q_heads * (S + prefix_states) * head_dim : nullptr;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
@@ -146,6 +197,8 @@ int prepare_decode(DecodeCall& call, const void* q, const void* k_cache, const v
   a.log2_block_size = log2_exact(block_size);
   a.split_tokens = split;
   a.num_splits = S;
+  a.ws_stride = S + prefix_states;
+  a.prefix_chunk = plan ? plan->chunk : 0;
   call.dtype = dtype;
   call.head_dim = head_dim;
   if (!pkv::row_attn_supported(dtype, head_dim, num_q_heads, num_kv_heads))
@@ -237,10 +290,22 @@ int32_t pkv_decode_split_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t n
 
 int64_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
                                    int32_t split_tokens) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0 || split_tokens <= 0) return 0;
+  if (max_context_len <= 0 || split_tokens <= 0) return 0;
   const int64_t S = (max_context_len + (int64_t)split_tokens - 1) / split_tokens;
-  if (S <= 1) return 0;
-  return (int64_t)num_seqs * num_q_heads * S * (head_dim + 2) * (int64_t)sizeof(float);
+  return state_bytes(num_seqs, num_q_heads, head_dim, S, 0);
+}
+
+int64_t pkv_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    int32_t max_context_len, int32_t max_own_len, int32_t split_tokens,
+                                    int32_t num_groups, int32_t max_group_size, int32_t max_shared_len) {
+  if (max_context_len <= 0 || split_tokens < 0 || max_shared_len < 0 || num_groups < 0 || num_q_heads <= 0 ||
+      num_kv_heads <= 0 || num_q_heads % num_kv_heads)
+    return 0;
+  const bool cascade = num_groups > 0 && max_shared_len > 0;
+  const DecodePlan p = cascade_plan(num_seqs, num_q_heads, num_kv_heads, max_context_len,
+                                    cascade ? max_own_len : 0, split_tokens, cascade ? num_groups : 0,
+                                    max_group_size, cascade ? max_shared_len : 0);
+  return state_bytes(num_seqs, num_q_heads, head_dim, p.S, p.C);
 }
 
 #define PKV_DECODE_ARGS                                                                                        \
@@ -278,6 +343,76 @@ int pkv_paged_decode_attn(PKV_DECODE_ARGS) {
   st = hip_status(pkv::launch_row_attn(call.args, call.dtype, call.head_dim, false, s), "decode split launch");
   if (st || call.args.num_splits <= 1) return st;
   return hip_status(pkv::launch_decode_reduce(call.args, call.dtype, call.head_dim, s), "decode reduce launch");
+}
+
+int pkv_cascade_decode_attn(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
+                            const int32_t* shared_lens, const int32_t* group_offsets, const int32_t* group_seqs,
+                            int32_t num_groups, int32_t max_group_size, int32_t max_shared_len, int32_t max_own_len,
+                            float scale, void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int64_t num_blocks, int32_t block_size, int32_t dtype,
+                            int32_t split_tokens, void* workspace, int64_t workspace_bytes, void* stream) {
+  if (num_groups < 0 || max_group_size < 0 || max_shared_len < 0 || max_own_len < 0)
+    return fail(PKV_ERR_INVALID_ARG, "negative group count, group size, shared length or own length");
+  const bool cascade = num_groups > 0 && max_shared_len > 0;
+  if (cascade) {
+    if (dtype != PKV_BF16)
+      return fail(PKV_ERR_UNSUPPORTED, "shared-prefix decode needs bf16 (its group pass runs on the matrix cores)");
+    if (!shared_lens || !group_offsets || !group_seqs)
+      return fail(PKV_ERR_INVALID_ARG, "null pointer among shared_lens, group_offsets, group_seqs");
+    if (max_group_size < 1) return fail(PKV_ERR_INVALID_ARG, "max_group_size %d < 1", max_group_size);
+    if (max_shared_len >= max_context_len)
+      return fail(PKV_ERR_INVALID_ARG, "max_shared_len %d must be below max_context_len %d", max_shared_len,
+                  max_context_len);
+    if (max_shared_len % block_size)
+      return fail(PKV_ERR_INVALID_ARG, "max_shared_len %d is not a whole number of blocks of %d", max_shared_len,
+                  block_size);
+  }
+  if (split_tokens < 0 || split_tokens % 64)
+    return fail(PKV_ERR_INVALID_ARG, "split_tokens %d is not 0 or a positive multiple of 64", split_tokens);
+  int st = check_heads(num_q_heads, num_kv_heads);
+  if (st) return st;
+  const DecodePlan plan = cascade_plan(num_seqs, num_q_heads, num_kv_heads, std::max(max_context_len, 1),
+                                       cascade ? max_own_len : 0, split_tokens, cascade ? num_groups : 0,
+                                       max_group_size, cascade ? max_shared_len : 0);
+  DecodeCall call;
+  st = prepare_decode(call, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                      scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, dtype,
+                      split_tokens, workspace, workspace_bytes, &plan);
+  if (st || call.empty) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  pkv::RowAttnArgs& r = call.args;
+  if (cascade) {
+    pkv::PrefillArgs g{};
+    g.q = q;
+    g.k = k_cache;
+    g.v = v_cache;
+    g.block_tables = block_tables;
+    g.scale_log2 = r.scale_log2;
+    g.num_seqs = num_seqs;
+    g.num_q_heads = num_q_heads;
+    g.num_kv_heads = num_kv_heads;
+    g.max_blocks_per_seq = max_blocks_per_seq;
+    g.log2_block_size = r.log2_block_size;
+    g.group_offsets = group_offsets;
+    g.group_seqs = group_seqs;
+    g.shared_lens = shared_lens;
+    g.ws_o = r.ws_o;
+    g.ws_ml = r.ws_ml;
+    g.ws_stride = r.ws_stride;
+    g.slot0 = r.num_splits;
+    g.chunk_tokens = plan.chunk;
+    g.num_groups = num_groups;
+    g.num_chunks = plan.C;
+    const int per_wg = pkv::shared_prefix_members_per_wg(num_q_heads, num_kv_heads);
+    g.member_tiles = (max_group_size + per_wg - 1) / per_wg;
+    st = hip_status(pkv::launch_shared_prefix_mfma(g, head_dim, s), "shared-prefix group pass launch");
+    if (st) return st;
+    r.kv_start = shared_lens;
+  }
+  st = hip_status(pkv::launch_row_attn(r, call.dtype, call.head_dim, false, s), "decode split launch");
+  if (st || (!cascade && r.num_splits <= 1)) return st;
+  return hip_status(pkv::launch_decode_reduce(r, call.dtype, call.head_dim, s), "decode reduce launch");
 }
 
 int pkv_paged_prefill_attn(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,

@@ -26,8 +26,14 @@ struct RowAttnArgs {
   const int32_t* cu_seqlens_q;  // prefill: [B + 1]
   const int32_t* cu_seqlens_k;  // prefill: [B + 1]
   void* out;
-  float* ws_o;   // [B, Hq, S, D] fp32 partial outputs (decode, S > 1)
-  float* ws_ml;  // [B, Hq, S, 2] fp32 (running max in log2 units, sum)
+  float* ws_o;   // [B, Hq, ws_stride, D] fp32 partial outputs (decode, S > 1 or shared prefixes)
+  float* ws_ml;  // [B, Hq, ws_stride, 2] fp32 (running max in log2 units, sum)
+  // Shared-prefix (cascade) decode: sequence b's keys [0, kv_start[b]) are
+  // attended by the group pass, which leaves ceil(kv_start[b] / prefix_chunk)
+  // states at slots num_splits .. of the pair; the split pass covers the rest.
+  const int32_t* kv_start;  // [B] or NULL (no shared prefixes)
+  int32_t ws_stride;        // state slots per (sequence, query head): num_splits + prefix chunks
+  int32_t prefix_chunk;     // keys per group-pass state
   float scale_log2;  // scale * log2(e)
   int32_t num_seqs;
   int32_t num_q_heads;
@@ -60,10 +66,35 @@ struct PrefillArgs {
   int32_t max_blocks_per_seq;
   int32_t log2_block_size;
   int32_t max_seqlen_q;
+  // Group pass of shared-prefix decode (q is [B, Hq, D]; NULL group_seqs = prefill):
+  // group gi's members are group_seqs[group_offsets[gi] ..], all sharing their
+  // first shared_lens[member] keys (same blocks); each workgroup takes up to
+  // 32 * (4 / heads per wave) members, one KV head's query heads and one chunk
+  // of chunk_tokens keys, and writes that chunk's softmax state per (member,
+  // head) at slot slot0 + chunk of the member's decode workspace.
+  const int32_t* group_offsets;
+  const int32_t* group_seqs;
+  const int32_t* shared_lens;
+  float* ws_o;
+  float* ws_ml;
+  int32_t ws_stride;
+  int32_t slot0;
+  int32_t chunk_tokens;
+  int32_t num_groups;
+  int32_t num_chunks;     // grid: ceil(max shared length / chunk_tokens)
+  int32_t member_tiles;   // grid: ceil(max group size / members per workgroup)
 };
 
 // bf16 matrix-core prefill.
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int32_t head_dim, hipStream_t stream);
+
+// bf16 matrix-core group pass of shared-prefix decode (same kernel, gathered queries).
+hipError_t launch_shared_prefix_mfma(const PrefillArgs& a, int32_t head_dim, hipStream_t stream);
+// Members per workgroup of the group pass for this head grouping.
+int shared_prefix_members_per_wg(int32_t num_q_heads, int32_t num_kv_heads);
+// Workgroups of the group pass per chunk of keys.
+int64_t shared_prefix_wgs_per_chunk(int32_t num_q_heads, int32_t num_kv_heads, int32_t num_groups,
+                                    int32_t max_group_size);
 
 // Arguments of the fused rotary embedding + cache write.
 struct RopeStoreArgs {

@@ -20,6 +20,15 @@
 //   order so no data moves between lanes.
 // Query i of a sequence sits at position Lk - Lq + i and sees keys <= it; the
 // mask is applied only on tiles that reach past a wave's first position.
+//
+// SHARED mode is the group pass of shared-prefix ("cascade") decode: the
+// columns are the decode queries of the members of one group (sequences
+// whose first keys are the same cached blocks), the keys one chunk of that
+// shared prefix, with no causal mask (every member's token comes after the
+// prefix), and the result is each column's unnormalised softmax state (m, l,
+// o) written to the member's decode workspace, merged later with the states
+// of its own keys.  The shared keys are thus read once per group instead of
+// once per member.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -43,7 +52,7 @@ __device__ __forceinline__ int vt_column(int k) {
   return (k & ~15) + ((k16 & 7) >> 2) * 8 + (k16 >> 3) * 4 + (k16 & 3);
 }
 
-template <int D, int HW, int NBW>
+template <int D, int HW, int NBW, bool SHARED>
 __global__ __launch_bounds__(256, NBW == 1 ? 2 : 1) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int PB = 4 / HW;           // position blocks (of 32 * NBW) per workgroup
   constexpr int WP = 32 * NBW;         // positions per wave
@@ -71,43 +80,71 @@ __global__ __launch_bounds__(256, NBW == 1 ? 2 : 1) void prefill_mfma_kernel(Pre
   int id = blockIdx.x;
   const int hg = id % NHG;
   id /= NHG;
-  const int b = id % a.num_seqs;
-  const int tile_rev = id / a.num_seqs;
-  const int q0 = a.cu_seqlens_q[b];
-  const int Lq = a.cu_seqlens_q[b + 1] - q0;
-  const int k0 = a.cu_seqlens_k[b];
-  const int Lk = a.cu_seqlens_k[b + 1] - k0;
-  const int n_qt = (Lq + QP - 1) / QP;
-  const int tile = n_qt - 1 - tile_rev;  // tiles with the most keys are dispatched first
-  if (tile < 0) return;
+  // Prefill: sequence b, its query tile `tile` (Lq queries, Lk keys, packed
+  // rows from k0).  Shared: group member tile `tile` (Lq members), keys
+  // [key_base, key_base + Lk) of the prefix, table row of the group's first
+  // member b.
+  int b, tile, q0 = 0, Lq, k0 = 0, Lk, key_base = 0, member0 = 0, chunk = 0;
+  if constexpr (SHARED) {
+    tile = id % a.member_tiles;
+    id /= a.member_tiles;
+    chunk = id % a.num_chunks;
+    const int gi = id / a.num_chunks;
+    member0 = a.group_offsets[gi];
+    Lq = a.group_offsets[gi + 1] - member0;
+    if (tile * QP >= Lq) return;
+    b = a.group_seqs[member0];
+    const int shared = a.shared_lens[b];
+    key_base = chunk * a.chunk_tokens;
+    if (key_base >= shared) return;
+    Lk = min(shared - key_base, a.chunk_tokens);
+  } else {
+    b = id % a.num_seqs;
+    const int tile_rev = id / a.num_seqs;
+    q0 = a.cu_seqlens_q[b];
+    Lq = a.cu_seqlens_q[b + 1] - q0;
+    k0 = a.cu_seqlens_k[b];
+    Lk = a.cu_seqlens_k[b + 1] - k0;
+    const int n_qt = (Lq + QP - 1) / QP;
+    tile = n_qt - 1 - tile_rev;  // tiles with the most keys are dispatched first
+    if (tile < 0) return;
+  }
 
   const int hl = wave % HW;
   const int pb = wave / HW;
   const int h = hg * HW + hl;
   const int g = (hg * HW) / G;
-  const int shift = Lk - Lq;  // position of query i is shift + i
+  // Positions are relative to key_base.  Prefill: query i sits at shift + i.
+  // Shared: every column sees the whole chunk, as a query at its last key.
+  const int shift = Lk - Lq;
   const int w_first = tile * QP + pb * WP;
   const int w_last = min(w_first + WP, Lq) - 1;
   const bool wave_active = w_first < Lq;
-  const int w_min_pos = shift + w_first;
-  const int w_max_pos = shift + w_last;
-  // column block nb of the wave holds queries w_first + 32 nb + col
+  const int w_min_pos = SHARED ? Lk - 1 : shift + w_first;
+  const int w_max_pos = SHARED ? Lk - 1 : shift + w_last;
+  // column block nb of the wave holds queries (members) w_first + 32 nb + col
   int pos[NBW];
   bool col_valid[NBW];
+  int64_t q_row[NBW];  // row of q[., Hq, D] (times Hq, plus the head)
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb) {
     const int qi = w_first + 32 * nb + col;
     col_valid[nb] = qi < Lq;
-    pos[nb] = col_valid[nb] ? shift + qi : Lk - 1;
+    pos[nb] = (col_valid[nb] && !SHARED) ? shift + qi : Lk - 1;
+    if constexpr (SHARED) {
+      q_row[nb] = col_valid[nb] ? (int64_t)a.group_seqs[member0 + qi] * Hq + h : 0;
+    } else {
+      q_row[nb] = (int64_t)(q0 + qi) * Hq + h;
+    }
   }
-  const int wg_max_pos = shift + min(tile * QP + QP, Lq) - 1;
+  const int wg_max_pos = SHARED ? Lk - 1 : shift + min(tile * QP + QP, Lq) - 1;
   const int n_kt = wg_max_pos / kKT + 1;
 
   // Q^T as the B operand: lane (col, half) holds Q[col][16 kk + 8 half .. +8].
   bf16x8_t qf[NBW][KSTEPS];
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb) {
-    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)(q0 + w_first + 32 * nb + col) * Hq + h) * D + 8 * half;
+    const uint16_t* qp = (const uint16_t*)a.q + q_row[nb] * D + 8 * half;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
       uint4 x = make_uint4(0, 0, 0, 0);
@@ -138,14 +175,14 @@ __global__ __launch_bounds__(256, NBW == 1 ? 2 : 1) void prefill_mfma_kernel(Pre
   // last key's row: their scores are masked (key > every position) and their
   // weights are exactly 0, so finite data suffices and no zero fill is needed.
   const int last_key = Lk - 1;
-  // block id holding key t (packed K/V: unused)
-  auto block_id = [&](int t) -> int32_t { return table ? table[min(t, last_key) >> lbs] : 0; };
+  // block id holding key t (relative to key_base; packed K/V: unused)
+  auto block_id = [&](int t) -> int32_t { return table ? table[(key_base + min(t, last_key)) >> lbs] : 0; };
   // element offset of key tc's row (tc <= last_key) for KV head g; blk is the block holding tc
   const int row_stride = Hkv * D;
   const int64_t blk_stride = (int64_t)row_stride << lbs;
   const int head_off = g * D;
   auto row_elem = [&](int tc, int32_t blk) -> int64_t {
-    if (table) return (int64_t)blk * blk_stride + ((tc & bs_mask) * row_stride + head_off);
+    if (table) return (int64_t)blk * blk_stride + (((key_base + tc) & bs_mask) * row_stride + head_off);
     return (int64_t)(k0 + tc) * row_stride + head_off;
   };
 
@@ -247,7 +284,7 @@ __global__ __launch_bounds__(256, NBW == 1 ? 2 : 1) void prefill_mfma_kernel(Pre
       // causal mask (only on tiles that reach past the block's first position):
       // key key0 + off(r) with off(r) = mb*32 + (r/4)*8 + half*4 + r%4 is
       // visible iff off(r) - half*4 <= pos - key0 - half*4
-      if (key0 + kKT - 1 > w_min_pos + 32 * nb) {
+      if (key0 + kKT - 1 > w_min_pos + (SHARED ? 0 : 32 * nb)) {
         const int lim = pos[nb] - key0 - half * 4;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
@@ -333,11 +370,34 @@ __global__ __launch_bounds__(256, NBW == 1 ? 2 : 1) void prefill_mfma_kernel(Pre
   }
 
   if (!wave_active) return;
+  if constexpr (SHARED) {
+    // unnormalised state of each column at slot slot0 + chunk of its member's pair
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+      const float l = halves_sum(lsum[nb]);
+      if (!col_valid[nb]) continue;
+      const int64_t slot = q_row[nb] * a.ws_stride + a.slot0 + chunk;
+      float* wo = a.ws_o + slot * D + half * 4;
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int r = rr * 4;
+          *reinterpret_cast<float4*>(wo + md * 32 + rr * 8) =
+              make_float4(acc_o[nb][md][r], acc_o[nb][md][r + 1], acc_o[nb][md][r + 2], acc_o[nb][md][r + 3]);
+        }
+      if (half == 0) {
+        a.ws_ml[slot * 2] = m[nb];
+        a.ws_ml[slot * 2 + 1] = l;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb) {
     if (!col_valid[nb]) continue;
     const float inv = 1.0f / halves_sum(lsum[nb]);
-    uint16_t* op = (uint16_t*)a.out + ((int64_t)(q0 + w_first + 32 * nb + col) * Hq + h) * D + half * 4;
+    uint16_t* op = (uint16_t*)a.out + q_row[nb] * D + half * 4;
 #pragma unroll
     for (int md = 0; md < MD; ++md) {
 #pragma unroll
@@ -354,19 +414,22 @@ __global__ __launch_bounds__(256, NBW == 1 ? 2 : 1) void prefill_mfma_kernel(Pre
 
 }  // namespace
 
-hipError_t launch_prefill_mfma(const PrefillArgs& a, int32_t head_dim, hipStream_t stream) {
-  const int G = a.num_q_heads / a.num_kv_heads;
-  const int HW = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+namespace {
+
+int heads_per_wave(int32_t num_q_heads, int32_t num_kv_heads) {
+  const int G = num_q_heads / num_kv_heads;
+  return (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+}
+
+template <bool SHARED>
+hipError_t launch(const PrefillArgs& a, int32_t head_dim, int64_t blocks, int HW, hipStream_t stream) {
   constexpr int NBW = PKV_PF_NBW;
-  const int QP = 32 * NBW * (4 / HW);
-  const int64_t n_qt = (a.max_seqlen_q + QP - 1) / QP;
-  const int64_t blocks = n_qt * a.num_seqs * (a.num_q_heads / HW);
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   dim3 grid((unsigned)blocks), block(256);
 #define PKV_PREFILL_CASE(DD, HH)                                                              \
   if (head_dim == DD && HW == HH) {                                                           \
-    hipLaunchKernelGGL((prefill_mfma_kernel<DD, HH, NBW>), grid, block, 0, stream, a);        \
+    hipLaunchKernelGGL((prefill_mfma_kernel<DD, HH, NBW, SHARED>), grid, block, 0, stream, a); \
     return hipGetLastError();                                                                 \
   }
   PKV_PREFILL_CASE(128, 4)
@@ -377,6 +440,32 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, int32_t head_dim, hipStream
   PKV_PREFILL_CASE(64, 1)
 #undef PKV_PREFILL_CASE
   return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_prefill_mfma(const PrefillArgs& a, int32_t head_dim, hipStream_t stream) {
+  const int HW = heads_per_wave(a.num_q_heads, a.num_kv_heads);
+  const int QP = 32 * PKV_PF_NBW * (4 / HW);
+  const int64_t n_qt = (a.max_seqlen_q + QP - 1) / QP;
+  return launch<false>(a, head_dim, n_qt * a.num_seqs * (a.num_q_heads / HW), HW, stream);
+}
+
+int shared_prefix_members_per_wg(int32_t num_q_heads, int32_t num_kv_heads) {
+  return 32 * PKV_PF_NBW * (4 / heads_per_wave(num_q_heads, num_kv_heads));
+}
+
+int64_t shared_prefix_wgs_per_chunk(int32_t num_q_heads, int32_t num_kv_heads, int32_t num_groups,
+                                    int32_t max_group_size) {
+  const int per_wg = shared_prefix_members_per_wg(num_q_heads, num_kv_heads);
+  const int64_t tiles = ((max_group_size > 1 ? max_group_size : 1) + per_wg - 1) / per_wg;
+  return (int64_t)num_groups * tiles * (num_q_heads / heads_per_wave(num_q_heads, num_kv_heads));
+}
+
+hipError_t launch_shared_prefix_mfma(const PrefillArgs& a, int32_t head_dim, hipStream_t stream) {
+  const int HW = heads_per_wave(a.num_q_heads, a.num_kv_heads);
+  const int64_t blocks = (int64_t)a.num_groups * a.num_chunks * a.member_tiles * (a.num_q_heads / HW);
+  return launch<true>(a, head_dim, blocks, HW, stream);
 }
 
 }  // namespace pkv

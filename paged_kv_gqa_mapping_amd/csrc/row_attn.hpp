@@ -113,10 +113,12 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
     t0 = 0;
     t1 = lk - lq + i + 1;
   } else {
+    // keys [0, start) of a sequence with a shared prefix belong to the group pass
     const int L = a.context_lens[b];
+    const int start = a.kv_start ? a.kv_start[b] : 0;
     split = j_or_row;
     q_row = b;
-    t0 = split * a.split_tokens;
+    t0 = start + split * a.split_tokens;
     if (L == 0) {
       if (split == 0) {  // an empty context gives zeros
         for (int gq = 0; gq < G; ++gq) {
@@ -129,7 +131,8 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
     }
     if (t0 >= L) return;
     t1 = min(L, t0 + a.split_tokens);
-    nsplit_b = (L + a.split_tokens - 1) / a.split_tokens;
+    // states merged for this row: its splits, plus the group pass's when it has a prefix
+    nsplit_b = (L - start + a.split_tokens - 1) / a.split_tokens + (start > 0 ? 1 : 0);
   }
 
   // Queries of the G heads sharing KV head g, in this lane's element order.
@@ -335,7 +338,7 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
       }
     }
   } else {
-    const int S = a.num_splits;
+    const int S = a.ws_stride;
     for (int gq = 0; gq < G; ++gq) {
       const int64_t slot = ((int64_t)b * Hq + g * G + gq) * S + split;
       float* wo = a.ws_o + slot * D;
@@ -353,7 +356,8 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
 
 // Merge the split states of each (sequence, query head): M = max_j m_j,
 // w_j = 2^(m_j - M), out = sum_j w_j o_j / sum_j w_j l_j.  One wave per pair,
-// splits merged in index order.
+// states merged in slot order: the pair's splits, then the group pass's
+// chunks of its shared prefix (if any).
 template <bool BF16, int D>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(RowAttnArgs a) {
   constexpr int EPL = D / 64;  // elements per lane
@@ -363,15 +367,20 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(RowAttnArgs a) {
   if (pair >= a.num_seqs * Hq) return;
   const int b = pair / Hq;
   const int L = a.context_lens[b];
-  const int ns = (L + a.split_tokens - 1) / a.split_tokens;
-  if (ns <= 1) return;
-  const int S = a.num_splits;
+  const int start = a.kv_start ? a.kv_start[b] : 0;
+  const int ns = (L - start + a.split_tokens - 1) / a.split_tokens;
+  const int np = start > 0 ? (start + a.prefix_chunk - 1) / a.prefix_chunk : 0;
+  if (np == 0 && ns <= 1) return;
+  const int S = a.ws_stride;
   const float* ml = a.ws_ml + (int64_t)pair * S * 2;
   const float* wo = a.ws_o + (int64_t)pair * S * D + lane * EPL;
+  // slot of the i-th state: splits 0 .. ns-1, then prefix chunks at num_splits ..
+  auto slot = [&](int i) { return i < ns ? i : a.num_splits + (i - ns); };
   float M = kNegInf;
-  for (int j = 0; j < ns; ++j) M = fmaxf(M, ml[2 * j]);
+  for (int i = 0; i < ns + np; ++i) M = fmaxf(M, ml[2 * slot(i)]);
   float den = 0.f, acc[EPL] = {};
-  for (int j = 0; j < ns; ++j) {
+  for (int i = 0; i < ns + np; ++i) {
+    const int j = slot(i);
     const float w = exp2_hw(ml[2 * j] - M);
     den = fmaf(w, ml[2 * j + 1], den);
     for (int e = 0; e < EPL; ++e) acc[e] = fmaf(w, wo[(int64_t)j * D + e], acc[e]);

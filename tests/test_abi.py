@@ -122,3 +122,44 @@ def test_rope_kv_store_argument_errors_before_launch():
     assert call(q=None) == -1
     assert call(k=p + 8) == -1           # misaligned
     assert call(N=0, q=None) == 0         # nothing to do: no launch, no pointer needed
+
+
+@needs_lib
+def test_cascade_argument_errors_before_launch():
+    L = pkv.lib()
+    p = 1 << 20
+
+    def call(**kw):
+        a = dict(q=p, k=p, v=p, bt=p, W=80, cl=p, maxL=17000, sh=p, go=p, gs=p, ng=1, gmax=64, smax=16384,
+                 own=600, scale=0.1, out=p, B=64, Hq=32, Hkv=8, D=128, NB=200, bs=256, dtype=1, split=0, ws=p,
+                 ws_bytes=1 << 40)
+        a.update(kw)
+        return L.pkv_cascade_decode_attn(a["q"], a["k"], a["v"], a["bt"], a["W"], a["cl"], a["maxL"], a["sh"],
+                                         a["go"], a["gs"], a["ng"], a["gmax"], a["smax"], a["own"], a["scale"],
+                                         a["out"], a["B"], a["Hq"], a["Hkv"], a["D"], a["NB"], a["bs"], a["dtype"],
+                                         a["split"], a["ws"], a["ws_bytes"], None)
+    assert call(dtype=0) == -2             # the group pass is bf16 only
+    assert call(smax=16384 + 3) == -1      # not whole blocks
+    assert call(smax=17000) == -1          # must leave every sequence a key of its own
+    assert call(ng=-1) == -1
+    assert call(own=-5) == -1
+    assert call(gmax=0) == -1
+    assert call(sh=None) == -1
+    assert call(split=100) == -1
+    assert call(ws=None) == -3             # workspace needed
+    assert call(ws_bytes=16) == -3
+    assert call(D=96) == -2
+
+
+@needs_lib
+def test_cascade_workspace_bytes():
+    L = pkv.lib()
+    # no groups: the plain decode workspace for the same split
+    for maxL, split in ((1000, 256), (20000, 512), (300, 512)):
+        assert L.pkv_cascade_workspace_bytes(64, 32, 8, 128, maxL, 0, split, 0, 0, 0) == \
+            L.pkv_decode_workspace_bytes(64, 32, 128, maxL, split)
+    # one group of 64 behind 16,384 shared keys with at most 512 keys of its own:
+    # 2 split states of 256 keys plus the group-pass states (chunk doubled from 256 while
+    # 2 member tiles x 8 head groups x chunks > 512 workgroups: 512 keys -> 32 chunks)
+    got = L.pkv_cascade_workspace_bytes(64, 32, 8, 128, 16896, 512, 256, 1, 64, 16384)
+    assert got == 64 * 32 * (2 + 32) * (128 + 2) * 4

@@ -246,6 +246,34 @@ def test_split_merge_identity(cuts):
     assert np.max(np.abs(merged - direct)) < 1e-12 * max(1.0, np.max(np.abs(direct)))
 
 
+def test_shared_prefix_states_merge_to_each_members_decode():
+    """Cascade reading of shared-prefix decode: the states of a group's shared
+    keys, taken once with all members' queries stacked, merged with each
+    member's states of its own keys, give each member's plain decode output."""
+    rng = np.random.default_rng(12)
+    bs, P, G, Hkv, D = 4, 3, 2, 2, 8
+    lens = [P * bs + 1, P * bs + 6, P * bs + 13]           # every member has keys beyond the prefix
+    q, kc, vc, bt, cl = _paged_case(12, 3, G * Hkv, Hkv, D, bs, lens)
+    bt[1, :P] = bt[0, :P]                                    # members 1 and 2 share member 0's prefix blocks
+    bt[2, :P] = bt[0, :P]
+    scale = 0.4
+    direct = oracle.decode(q, kc, vc, bt, cl, scale, "f32", bs)
+    qw = oracle.widen(q, "f32")
+    K0 = oracle.widen(oracle.gather(kc, bt[0], P * bs, bs), "f32")
+    V0 = oracle.widen(oracle.gather(vc, bt[0], P * bs, bs), "f32")
+    for g in range(Hkv):
+        heads = slice(g * G, (g + 1) * G)
+        stacked = qw[:, heads].reshape(-1, D)                # every member's query heads of KV head g
+        chunks = [oracle.partial_state(stacked, K0[a:a + 4, g], V0[a:a + 4, g], scale) for a in range(0, P * bs, 4)]
+        for b in range(3):
+            K = oracle.widen(oracle.gather(kc, bt[b], int(cl[b]), bs), "f32")[P * bs:, g]
+            V = oracle.widen(oracle.gather(vc, bt[b], int(cl[b]), bs), "f32")[P * bs:, g]
+            rows = slice(b * G, (b + 1) * G)
+            mine = [(m[rows], l[rows], o[rows]) for m, l, o in chunks]
+            merged = oracle.merge_states([oracle.partial_state(qw[b, heads], K, V, scale)] + mine)
+            assert np.max(np.abs(merged - direct[b, heads])) < 1e-12
+
+
 def test_kv_store_matches_flat_indexing_and_touches_nothing_else():
     rng = np.random.default_rng(10)
     nb, bs, hkv, d = 6, 4, 2, 8

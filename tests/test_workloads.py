@@ -46,7 +46,7 @@ def _check_common(w):
             assert np.isfinite(W.to_float32(rows, w.dtype)).all()
 
 
-@pytest.mark.parametrize("i", [1, 2, 4])
+@pytest.mark.parametrize("i", [1, 2, 4, 6])
 def test_config_metadata(i):
     w = W.make_config(i)
     _check_common(w)
@@ -117,3 +117,29 @@ def test_small_mixed_step_layout():
     _check_common(w)
     assert len(w.slot_mapping) == 512 + 512 + 4
     assert (w.refcount[w.shared_blocks] == 2).all()
+
+
+def test_config6_shared_prompt_and_cascade_groups():
+    w = W.make_config(6)
+    assert len(w.shared_blocks) == 64 and (w.refcount[w.shared_blocks] == 64).all()
+    assert (w.dec_block_tables[:, :64] == np.asarray(w.shared_blocks)).all()
+    shared, offsets, seqs, gmax, smax, own = w.cascade_groups()
+    assert own == int((w.dec_context_lens - 16384).max())
+    assert (shared == 64 * 256).all() and list(offsets) == [0, 64] and sorted(seqs) == list(range(64))
+    assert (gmax, smax) == (64, 16384)
+    suffix = w.dec_context_lens - 16384
+    assert suffix.min() >= 1 and suffix.max() <= 512
+    # unique bytes: the prompt once plus every sequence's own tokens
+    row = 2 * w.num_kv_heads * w.head_dim * 2
+    assert w.decode_kv_bytes_unique() == (16384 + int(suffix.sum())) * row
+    assert w.decode_kv_bytes() == int(w.dec_context_lens.sum()) * row
+    capped = w.cascade_groups(group_cap=10)
+    assert list(capped[1]) == [0, 10, 20, 30, 40, 50, 60, 64] and capped[3] == 10
+
+
+def test_cascade_groups_of_config5():
+    w = W.make_config(5)
+    shared, offsets, seqs, gmax, smax, own = w.cascade_groups()
+    assert own == int(w.dec_context_lens.max())  # the longest context has no shared prefix
+    assert list(offsets) == [0, 50] and sorted(seqs) == w.notes["sharers"] and smax == 4096
+    assert (shared[seqs] == 4096).all() and (np.delete(shared, seqs) == 0).all()

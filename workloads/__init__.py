@@ -234,6 +234,36 @@ class Workload:
             return 0
         return int(self.dec_context_lens.astype(np.int64).sum()) * 2 * self.num_kv_heads * self.head_dim * self.elt_bytes
 
+    def decode_kv_bytes_unique(self) -> int:
+        """As decode_kv_bytes, with each decode sequence's shared prefix blocks counted once
+        per distinct shared length (what shared-prefix decode reads)."""
+        if self.dec_context_lens is None:
+            return 0
+        dec = [s for s in self.seqs if s.kind == "decode"]
+        tokens = int(self.dec_context_lens.astype(np.int64).sum())
+        shared = [s.shared * self.block_size for s in dec]
+        tokens -= sum(shared)
+        tokens += sum(set(x for x in shared if x > 0))
+        return tokens * 2 * self.num_kv_heads * self.head_dim * self.elt_bytes
+
+    def cascade_groups(self, group_cap: int | None = None):
+        """Shared-prefix groups of the decode sequences (those taking the same number
+        of leading shared blocks form a group, cut into groups of at most group_cap):
+        (shared_lens [B] int32 in tokens, group_offsets int32, group_seqs int32,
+        max_group_size, max_shared_len, max_own_len), the last being the longest
+        context_len - shared_len."""
+        dec = [s for s in self.seqs if s.kind == "decode"]
+        shared = np.array([s.shared * self.block_size for s in dec], dtype=np.int32)
+        groups = []
+        for n in sorted(set(int(x) for x in shared if x > 0)):
+            members = [j for j in range(len(dec)) if shared[j] == n]
+            cap = group_cap or len(members)
+            groups += [members[i:i + cap] for i in range(0, len(members), cap)]
+        offsets = np.concatenate([[0], np.cumsum([len(g) for g in groups])]).astype(np.int32)
+        seqs = np.array([j for g in groups for j in g], dtype=np.int32)
+        own = int((self.dec_context_lens - shared).max(initial=0))
+        return shared, offsets, seqs, max([len(g) for g in groups] + [0]), int(shared.max(initial=0)), own
+
     def decode_io_bytes(self) -> int:
         """q read + out written by the decode step."""
         if self.dec_q is None:
@@ -410,11 +440,12 @@ CONFIG_NAMES = {
     3: "llama8b-long-decode-splitk-bf16",
     4: "prefix-cached-varlen-prefill-bf16",
     5: "mixed-continuous-batching-step-bf16",
+    6: "shared-prompt-decode-bf16",
 }
 
 
 def make_config(i: int, seed: int | None = None, poison: str = "nan", dtype: str | None = None) -> Workload:
-    """Workload i (1..5).  ``dtype`` overrides the element type (the same shapes
+    """Workload i (1..6).  ``dtype`` overrides the element type (the same shapes
     in fp32 let a 1e-5 tolerance see a single misplaced key at long context)."""
     seed = i if seed is None else seed
     rng = np.random.default_rng(seed)
@@ -452,6 +483,14 @@ def make_config(i: int, seed: int | None = None, poison: str = "nan", dtype: str
         w = build(name, seed, dt, 32, 8, 128, 256, seqs, shared_prefix_blocks=16, table_width_decode=128,
                   table_width_prefill=34, perm_rng=rng, poison=poison)
         w.notes["sharers"] = sorted(sharers)
+        return w
+    if i == 6:
+        # shared-prefix decode: 64 sequences behind one cached 16,384-token prompt
+        # (64 blocks of 256, refcount 64), each with U{1..512} tokens of its own
+        suffix = rng.integers(1, 512, size=64, endpoint=True)
+        seqs = [SeqSpec("decode", 64 * 256 + int(s), 1, shared=64) for s in suffix]
+        w = build(name, seed, dt, 32, 8, 128, 256, seqs, shared_prefix_blocks=64, perm_rng=rng, poison=poison)
+        w.notes["sharers"] = list(range(64))
         return w
     raise ValueError(f"no config {i}")
 
