@@ -38,6 +38,12 @@
 #define PKV_PF_NBW 1
 #endif
 
+// Tiles of K/V whose global loads are in flight while a tile is computed (1 or
+// 2 register stages).
+#ifndef PKV_PF_DEPTH
+#define PKV_PF_DEPTH 2
+#endif
+
 namespace pkv {
 
 namespace {
@@ -52,7 +58,10 @@ __device__ __forceinline__ int vt_column(int k) {
   return (k & ~15) + ((k16 & 7) >> 2) * 8 + (k16 >> 3) * 4 + (k16 & 3);
 }
 
-template <int D, int HW, int NBW, bool SHARED>
+// UT: every 64-key tile lies in one block (block_size >= 64, or packed K/V), so
+// a tile's base address is the same for the whole wave and only the row within
+// the tile is per lane.
+template <int D, int HW, int NBW, bool SHARED, bool UT>
 __global__ __launch_bounds__(256, NBW == 1 ? 2 : 1) void prefill_mfma_kernel(PrefillArgs a) {
   constexpr int PB = 4 / HW;           // position blocks (of 32 * NBW) per workgroup
   constexpr int WP = 32 * NBW;         // positions per wave
@@ -177,6 +186,8 @@ __global__ __launch_bounds__(256, NBW == 1 ? 2 : 1) void prefill_mfma_kernel(Pre
   const int last_key = Lk - 1;
   // block id holding key t (relative to key_base; packed K/V: unused)
   auto block_id = [&](int t) -> int32_t { return table ? table[(key_base + min(t, last_key)) >> lbs] : 0; };
+  // UT: block id of the tile starting at key t (t <= last_key), the same for every lane
+  auto tile_block = [&](int t) -> int32_t { return table ? uniform(table[(key_base + t) >> lbs]) : 0; };
   // element offset of key tc's row (tc <= last_key) for KV head g; blk is the block holding tc
   const int row_stride = Hkv * D;
   const int64_t blk_stride = (int64_t)row_stride << lbs;
@@ -187,10 +198,34 @@ __global__ __launch_bounds__(256, NBW == 1 ? 2 : 1) void prefill_mfma_kernel(Pre
   };
 
   static_assert(CPT == 2 || CPT == 4, "head_dim 64 or 128");
-  // prefetched rows, as separate values so that they stay in registers
-  uint4 k0r, k1r, k2r, k3r;  // K chunks k_c0 + 4 i, i < CPT
-  uint4 v0, v1, v2, v3;      // V rows of keys 4 kg .. 4 kg + 3
-  auto issue_loads = [&](int kt, int32_t bk, int32_t bv) {
+  // Prefetched rows of one tile (a stage): K chunks k_c0 + 4 i (i < CPT) and
+  // the V rows of keys 4 kg .. 4 kg + 3, passed as separate values so that
+  // they stay in registers.
+#define PKV_STAGE_PARAMS uint4 &k0r, uint4 &k1r, uint4 &k2r, uint4 &k3r, uint4 &v0, uint4 &v1, uint4 &v2, uint4 &v3
+  auto issue_loads = [&](PKV_STAGE_PARAMS, int kt, int32_t bk, int32_t bv) {
+    if constexpr (UT) {
+      // bk is the tile's block; rows past the end re-read the last key's row
+      const int t0 = kt * kKT;
+      const int64_t tile = table ? (int64_t)bk * blk_stride + (int64_t)((key_base + t0) & bs_mask) * row_stride
+                                 : (int64_t)(k0 + t0) * row_stride;
+      const int last = last_key - t0;
+      const uint16_t* kp = kbase + tile + (min(k_row, last) * row_stride + head_off + k_c0 * 8);
+      k0r = *reinterpret_cast<const uint4*>(kp);
+      k1r = *reinterpret_cast<const uint4*>(kp + 32);
+      if constexpr (CPT == 4) {
+        k2r = *reinterpret_cast<const uint4*>(kp + 64);
+        k3r = *reinterpret_cast<const uint4*>(kp + 96);
+      }
+      if (v_loader) {
+        const uint16_t* vp = vbase + tile + (head_off + v_dc * 8);
+        const int tv = 4 * v_kg;
+        v0 = *reinterpret_cast<const uint4*>(vp + min(tv, last) * row_stride);
+        v1 = *reinterpret_cast<const uint4*>(vp + min(tv + 1, last) * row_stride);
+        v2 = *reinterpret_cast<const uint4*>(vp + min(tv + 2, last) * row_stride);
+        v3 = *reinterpret_cast<const uint4*>(vp + min(tv + 3, last) * row_stride);
+      }
+      return;
+    }
     const int64_t ek = row_elem(min(kt * kKT + k_row, last_key), bk) + k_c0 * 8;
     k0r = *reinterpret_cast<const uint4*>(kbase + ek);
     k1r = *reinterpret_cast<const uint4*>(kbase + ek + 32);
@@ -213,7 +248,7 @@ __global__ __launch_bounds__(256, NBW == 1 ? 2 : 1) void prefill_mfma_kernel(Pre
       v3 = row(3);
     }
   };
-  auto write_lds = [&](int buf) {
+  auto write_lds = [&](PKV_STAGE_PARAMS, int buf) {
     uint16_t* kd = &lds_k[buf][k_row * KS + k_c0 * 8];
     *reinterpret_cast<uint4*>(kd) = k0r;
     *reinterpret_cast<uint4*>(kd + 32) = k1r;
@@ -334,40 +369,95 @@ __global__ __launch_bounds__(256, NBW == 1 ? 2 : 1) void prefill_mfma_kernel(Pre
     }
   };
 
-  // Pipeline: tile kt+1's global loads are in flight while tile kt is computed
-  // from LDS; block ids run two tiles ahead.  One barrier per tile.  The
-  // tiles past this wave's last position are only loaded for the other waves
-  // (second loop), which keeps the compute loop free of a data-dependent skip.
-  int32_t bk = block_id(k_row), bv = block_id(4 * v_kg);
-  issue_loads(0, bk, bv);
+  const int n_kt_wave = wave_active ? min(n_kt, w_max_pos / kKT + 1) : 0;
+  // block ids of the next tile to load (run one tile ahead of its loads)
+  int32_t bk, bv = 0;
+  auto next_ids = [&](int t) {
+    if constexpr (UT) {
+      bk = tile_block(t * kKT);
+    } else {
+      bk = block_id(t * kKT + k_row);
+      bv = block_id(t * kKT + 4 * v_kg);
+    }
+  };
+  next_ids(0);
+#if PKV_PF_DEPTH == 2
+  // Pipeline: while tile kt is computed from LDS, the global loads of tiles
+  // kt+1 and kt+2 are in flight in two register stages (tile t in stage t % 2),
+  // so a load has two tiles' compute time to arrive.  One barrier per tile.
+  // The tiles past this wave's last position are only loaded for the other
+  // waves (the last loop), which keeps the compute loop free of a
+  // data-dependent skip.
+  uint4 a0, a1, a2, a3, a4, a5, a6, a7;  // stage 0
+  uint4 b0, b1, b2, b3, b4, b5, b6, b7;  // stage 1
+#define PKV_S0 a0, a1, a2, a3, a4, a5, a6, a7
+#define PKV_S1 b0, b1, b2, b3, b4, b5, b6, b7
+  issue_loads(PKV_S0, 0, bk, bv);
   if (n_kt > 1) {
-    bk = block_id(kKT + k_row);
-    bv = block_id(kKT + 4 * v_kg);
+    next_ids(1);
+    issue_loads(PKV_S1, 1, bk, bv);
+    if (n_kt > 2) next_ids(2);
   }
-  write_lds(0);
+  write_lds(PKV_S0, 0);
+  __syncthreads();
+  if (n_kt > 2) {
+    issue_loads(PKV_S0, 2, bk, bv);
+    if (n_kt > 3) next_ids(3);
+  }
+  // tile kt: compute it, move tile kt+1 from its stage `wr` to LDS, refill `wr` with tile kt+3
+  auto step = [&](int kt, PKV_STAGE_PARAMS, bool with_compute) {
+    if (with_compute) compute(kt & 1, kt * kKT);
+    if (kt + 1 < n_kt) write_lds(k0r, k1r, k2r, k3r, v0, v1, v2, v3, (kt & 1) ^ 1);
+    if (kt + 3 < n_kt) {
+      issue_loads(k0r, k1r, k2r, k3r, v0, v1, v2, v3, kt + 3, bk, bv);
+      if (kt + 4 < n_kt) next_ids(kt + 4);
+    }
+    __syncthreads();
+  };
+  int kt = 0;
+  for (; kt + 1 < n_kt_wave; kt += 2) {
+    step(kt, PKV_S1, true);
+    step(kt + 1, PKV_S0, true);
+  }
+  if (kt < n_kt_wave) step(kt++, PKV_S1, true);
+  for (; kt < n_kt; ++kt) {
+    if (kt & 1)
+      step(kt, PKV_S0, false);
+    else
+      step(kt, PKV_S1, false);
+  }
+#undef PKV_S0
+#undef PKV_S1
+#else
+  // Pipeline: tile kt+1's global loads are in flight while tile kt is computed
+  // from LDS; block ids run two tiles ahead.  One barrier per tile.
+  uint4 a0, a1, a2, a3, a4, a5, a6, a7;
+#define PKV_S0 a0, a1, a2, a3, a4, a5, a6, a7
+  issue_loads(PKV_S0, 0, bk, bv);
+  if (n_kt > 1) next_ids(1);
+  write_lds(PKV_S0, 0);
   __syncthreads();
   auto advance = [&](int kt) {
     if (kt + 1 < n_kt) {
-      issue_loads(kt + 1, bk, bv);
-      if (kt + 2 < n_kt) {
-        bk = block_id((kt + 2) * kKT + k_row);
-        bv = block_id((kt + 2) * kKT + 4 * v_kg);
-      }
+      issue_loads(PKV_S0, kt + 1, bk, bv);
+      if (kt + 2 < n_kt) next_ids(kt + 2);
     }
   };
-  const int n_kt_wave = wave_active ? min(n_kt, w_max_pos / kKT + 1) : 0;
   int kt = 0;
   for (; kt < n_kt_wave; ++kt) {
     advance(kt);
     compute(kt & 1, kt * kKT);
-    if (kt + 1 < n_kt) write_lds((kt & 1) ^ 1);
+    if (kt + 1 < n_kt) write_lds(PKV_S0, (kt & 1) ^ 1);
     __syncthreads();
   }
   for (; kt < n_kt; ++kt) {
     advance(kt);
-    if (kt + 1 < n_kt) write_lds((kt & 1) ^ 1);
+    if (kt + 1 < n_kt) write_lds(PKV_S0, (kt & 1) ^ 1);
     __syncthreads();
   }
+#undef PKV_S0
+#endif
+#undef PKV_STAGE_PARAMS
 
   if (!wave_active) return;
   if constexpr (SHARED) {
@@ -427,10 +517,14 @@ hipError_t launch(const PrefillArgs& a, int32_t head_dim, int64_t blocks, int HW
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   dim3 grid((unsigned)blocks), block(256);
-#define PKV_PREFILL_CASE(DD, HH)                                                              \
-  if (head_dim == DD && HW == HH) {                                                           \
-    hipLaunchKernelGGL((prefill_mfma_kernel<DD, HH, NBW, SHARED>), grid, block, 0, stream, a); \
-    return hipGetLastError();                                                                 \
+  const bool ut = !a.block_tables || a.log2_block_size >= 6;  // a 64-key tile never crosses a block
+#define PKV_PREFILL_CASE(DD, HH)                                                                      \
+  if (head_dim == DD && HW == HH) {                                                                   \
+    if (ut)                                                                                           \
+      hipLaunchKernelGGL((prefill_mfma_kernel<DD, HH, NBW, SHARED, true>), grid, block, 0, stream, a);  \
+    else                                                                                              \
+      hipLaunchKernelGGL((prefill_mfma_kernel<DD, HH, NBW, SHARED, false>), grid, block, 0, stream, a); \
+    return hipGetLastError();                                                                         \
   }
   PKV_PREFILL_CASE(128, 4)
   PKV_PREFILL_CASE(128, 2)
