@@ -346,6 +346,55 @@ int32_t pkv_bm_block_table(pkv_block_manager* bm, int64_t seq_id, int32_t* out, 
 /* Slots of positions first_pos .. first_pos + count - 1 of a sequence. */
 int pkv_bm_slot_mapping(pkv_block_manager* bm, int64_t seq_id, int64_t first_pos, int64_t count, int32_t* out);
 
+/*
+ * Precondition checks.  The attention calls check every argument they can on
+ * the host, but their device-side preconditions (block ids inside the pool,
+ * lengths within the stated maxima, cu_seqlens ordered with Lq <= Lk, slots
+ * inside the pool and distinct, consistent shared-prefix groups) are the
+ * caller's: breaking one gives undefined results, possibly a memory fault.
+ * These calls test them on the device without touching the caches (they read
+ * only the metadata arrays, so they are safe on any input) and leave in
+ * `flags` (device int32[PKV_CHECK_NUM_FLAGS], zeroed by the call) the number
+ * of violations of each kind.  Asynchronous like every call: read `flags`
+ * after synchronizing the stream.  They check exactly the conditions of the
+ * matching attention call with the same arguments.
+ */
+typedef enum {
+  PKV_CHECK_LENGTH = 0,         /* a context or key count outside [0, max], or more blocks than a table row holds */
+  PKV_CHECK_BLOCK_ID = 1,       /* a block id outside [0, num_blocks) among the blocks a sequence uses */
+  PKV_CHECK_CU_SEQLENS = 2,     /* cu_seqlens not starting at 0 or decreasing, Lq > Lk, or above the maxima */
+  PKV_CHECK_SLOT = 3,           /* a slot >= num_blocks * block_size */
+  PKV_CHECK_DUPLICATE_SLOT = 4, /* a slot named by two tokens (only with a bitmap) */
+  PKV_CHECK_SHARED_PREFIX = 5,  /* a member whose shared length or shared block ids differ from its group's,
+                                   not whole blocks, not below its context, or above max_shared_len */
+  PKV_CHECK_GROUP = 6,          /* bad group offsets or member index, or a sequence in no group (with a shared
+                                   length) or in several */
+  PKV_CHECK_NUM_FLAGS = 8
+} pkv_check_flag;
+
+/* Preconditions of pkv_paged_decode_attn (and of the cascade call's tables). */
+int pkv_check_decode_inputs(const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t max_context_len, int32_t num_seqs, int64_t num_blocks, int32_t block_size,
+                            int32_t* flags, void* stream);
+
+/* Preconditions of pkv_paged_prefill_attn (block_tables NULL: packed k/v, no block check). */
+int pkv_check_prefill_inputs(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                             int64_t num_blocks, int32_t block_size, int32_t* flags, void* stream);
+
+/* Preconditions of pkv_kv_store / pkv_rope_kv_store.  bitmap: NULL (no duplicate
+ * check) or device uint32[ceil(num_blocks * block_size / 32)], overwritten. */
+int pkv_check_slots(const int32_t* slot_mapping, int64_t num_tokens, int64_t num_blocks, int32_t block_size,
+                    uint32_t* bitmap, int32_t* flags, void* stream);
+
+/* Group preconditions of pkv_cascade_decode_attn (run pkv_check_decode_inputs
+ * for its tables).  num_members = entries of group_seqs; seen: device
+ * int32[num_seqs], overwritten. */
+int pkv_check_cascade_inputs(const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                             const int32_t* shared_lens, const int32_t* group_offsets, const int32_t* group_seqs,
+                             int32_t num_groups, int32_t num_members, int32_t num_seqs, int32_t max_group_size,
+                             int32_t max_shared_len, int32_t block_size, int32_t* seen, int32_t* flags, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

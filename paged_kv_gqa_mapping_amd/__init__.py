@@ -12,6 +12,14 @@ Entry points (names follow the operations of a nano-vLLM style engine):
 * ``paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, scale, out)``
 * ``paged_prefill_attn(q, k, v, cu_seqlens_q, cu_seqlens_k, block_tables, out)``
 * ``paged_gather(k_cache, v_cache, block_tables, cu_seqlens_k)``
+* ``rope_kv_store(q, k, v, positions, k_cache, v_cache, slot_mapping, rope_theta)``
+* ``cascade_decode_attn(q, k_cache, v_cache, block_tables, context_lens, shared_lens,
+  group_offsets, group_seqs, scale, out)``
+* ``check_decode_inputs``, ``check_prefill_inputs``, ``check_slots``,
+  ``check_cascade_inputs``: device-side precondition checks (counts per kind).
+  With the environment variable ``PKV_DEBUG_CHECKS=1`` every call runs the
+  matching checks first and raises ``PkvError`` on a violation (this
+  synchronizes, so it is for debugging, not for graph capture).
 
 Tensors: caches ``[num_blocks, block_size, num_kv_heads, head_dim]``;
 ``torch.bfloat16`` or ``torch.float32``; metadata ``torch.int32``; all on the
@@ -29,6 +37,13 @@ __all__ = [
     "paged_decode_reduce",
     "paged_prefill_attn",
     "paged_gather",
+    "rope_kv_store",
+    "cascade_decode_attn",
+    "cascade_workspace_bytes",
+    "check_decode_inputs",
+    "check_prefill_inputs",
+    "check_slots",
+    "check_cascade_inputs",
     "decode_split_tokens",
     "decode_workspace_bytes",
     "lib",
@@ -45,6 +60,11 @@ PKV_F32 = 0
 PKV_BF16 = 1
 
 _lib = None
+
+# Run the device-side precondition checks before every call (debugging aid).
+DEBUG_CHECKS = os.environ.get("PKV_DEBUG_CHECKS", "") not in ("", "0")
+CHECK_NAMES = ("length", "block_id", "cu_seqlens", "slot", "duplicate_slot", "shared_prefix", "group")
+_NUM_FLAGS = 8
 
 
 class PkvError(RuntimeError):
@@ -77,6 +97,13 @@ def lib() -> ctypes.CDLL:
     L.pkv_cascade_decode_attn.restype = ctypes.c_int
     L.pkv_cascade_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32, I32, I32]
     L.pkv_cascade_workspace_bytes.restype = I64
+    L.pkv_check_decode_inputs.argtypes = [P, I32, P, I32, I32, I64, I32, P, V]
+    L.pkv_check_prefill_inputs.argtypes = [P, P, P, I32, I32, I32, I32, I64, I32, P, V]
+    L.pkv_check_slots.argtypes = [P, I64, I64, I32, P, P, V]
+    L.pkv_check_cascade_inputs.argtypes = [P, I32, P, P, P, P, I32, I32, I32, I32, I32, I32, P, P, V]
+    for name in ("pkv_check_decode_inputs", "pkv_check_prefill_inputs", "pkv_check_slots",
+                 "pkv_check_cascade_inputs"):
+        getattr(L, name).restype = ctypes.c_int
     L.pkv_decode_split_tokens.argtypes = [I32, I32, I32, I32, I32, I32, I32]
     L.pkv_decode_split_tokens.restype = I32
     L.pkv_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
@@ -173,6 +200,8 @@ def kv_store(k, v, k_cache, v_cache, slot_mapping) -> None:
     NB, bs, Hkv2, D2 = k_cache.shape
     if v.shape != k.shape or v_cache.shape != k_cache.shape or (Hkv2, D2) != (Hkv, D) or slot_mapping.shape[0] != N:
         raise ValueError("shape mismatch among k, v, k_cache, v_cache, slot_mapping")
+    if DEBUG_CHECKS:
+        _require(check_slots(slot_mapping, NB, bs), "kv_store")
     _check(lib().pkv_kv_store(_ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), N, Hkv, D, NB, bs,
                               _dtype_code(k), _stream()))
 
@@ -194,6 +223,8 @@ def rope_kv_store(q, k, v, positions, k_cache, v_cache, slot_mapping, rope_theta
     if (k.shape != (N, Hkv, D) or v.shape != k.shape or v_cache.shape != k_cache.shape or (Hkv2, D2) != (Hkv, D)
             or positions.shape[0] != N or slot_mapping.shape[0] != N):
         raise ValueError("shape mismatch among q, k, v, positions, k_cache, v_cache, slot_mapping")
+    if DEBUG_CHECKS:
+        _require(check_slots(slot_mapping, NB, bs), "rope_kv_store")
     _check(lib().pkv_rope_kv_store(_ptr(q), _ptr(k), _ptr(v), _ptr(positions), _ptr(k_cache), _ptr(v_cache),
                                    _ptr(slot_mapping), N, Hq, Hkv, D, NB, bs, float(rope_theta), int(bool(interleaved)),
                                    _dtype_code(q), _stream()))
@@ -231,6 +262,8 @@ def _decode(fn_name, q, k_cache, v_cache, block_tables, context_lens, scale, out
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if DEBUG_CHECKS:
+        _require(check_decode_inputs(block_tables, context_lens, max_context_len, NB, bs), fn_name)
     _check(getattr(lib(), fn_name)(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
         int(max_context_len), float(scale), _ptr(out), B, Hq, Hkv, D, NB, bs, code, split, _ptr(workspace), ws_bytes,
@@ -300,6 +333,11 @@ def cascade_decode_attn(q, k_cache, v_cache, block_tables, context_lens, shared_
                                    max_shared_len)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if DEBUG_CHECKS:
+        _require(check_decode_inputs(block_tables, context_lens, max_context_len, NB, bs), "cascade_decode_attn")
+        if num_groups > 0:
+            _require(check_cascade_inputs(block_tables, context_lens, shared_lens, group_offsets, group_seqs,
+                                          max_group_size, max_shared_len, bs), "cascade_decode_attn")
     _check(lib().pkv_cascade_decode_attn(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
         max_context_len, _ptr(shared_lens), _ptr(group_offsets), _ptr(group_seqs), num_groups, max_group_size,
@@ -341,10 +379,95 @@ def paged_prefill_attn(q, k, v, cu_seqlens_q, cu_seqlens_k, block_tables, out, m
         max_seqlen_q = int((cq[1:] - cq[:-1]).max()) if B else 0
         max_seqlen_k = int((ck[1:] - ck[:-1]).max()) if B else 0
     sc = 0.0 if scale is None else float(scale)
+    if DEBUG_CHECKS:
+        _require(check_prefill_inputs(cu_seqlens_q, cu_seqlens_k, block_tables, max_seqlen_q, max_seqlen_k, NB,
+                                      bs if block_tables is not None else 1), "paged_prefill_attn")
     _check(lib().pkv_paged_prefill_attn(
         _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(block_tables), W, _ptr(out), sc, B,
         Tq, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D, NB, bs, _dtype_code(q), _stream()))
     return out
+
+
+# ---------------------------------------------------------------- precondition checks
+
+
+def _flags(device):
+    return _torch().zeros(_NUM_FLAGS, dtype=_torch().int32, device=device)
+
+
+def _counts(flags) -> dict:
+    vals = flags.cpu().tolist()  # synchronizes
+    return {n: int(vals[i]) for i, n in enumerate(CHECK_NAMES)}
+
+
+def _require(counts: dict, what: str) -> None:
+    bad = {k: v for k, v in counts.items() if v}
+    if bad:
+        raise PkvError(f"{what}: device-side precondition violated: {bad}")
+
+
+def check_decode_inputs(block_tables, context_lens, max_context_len, num_blocks, block_size) -> dict:
+    """Violations (per kind) of decode's preconditions: context lengths within
+    [0, max_context_len] and the block ids they use inside [0, num_blocks)."""
+    torch = _torch()
+    _dev(block_tables, "block_tables", torch.int32, 2)
+    _dev(context_lens, "context_lens", torch.int32, 1)
+    f = _flags(block_tables.device)
+    _check(lib().pkv_check_decode_inputs(_ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+                                         int(max_context_len), context_lens.shape[0], int(num_blocks), int(block_size),
+                                         _ptr(f), _stream()))
+    return _counts(f)
+
+
+def check_prefill_inputs(cu_seqlens_q, cu_seqlens_k, block_tables, max_seqlen_q, max_seqlen_k, num_blocks,
+                         block_size) -> dict:
+    """Violations of prefill's preconditions (cu_seqlens from 0, ordered, Lq <= Lk, within
+    the maxima; with block tables, the block ids holding each sequence's keys)."""
+    torch = _torch()
+    _dev(cu_seqlens_q, "cu_seqlens_q", torch.int32, 1)
+    _dev(cu_seqlens_k, "cu_seqlens_k", torch.int32, 1)
+    W = 0
+    if block_tables is not None:
+        _dev(block_tables, "block_tables", torch.int32, 2)
+        W = block_tables.shape[1]
+    f = _flags(cu_seqlens_q.device)
+    _check(lib().pkv_check_prefill_inputs(_ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(block_tables), W,
+                                          cu_seqlens_q.shape[0] - 1, int(max_seqlen_q), int(max_seqlen_k),
+                                          int(num_blocks), int(block_size), _ptr(f), _stream()))
+    return _counts(f)
+
+
+def check_slots(slot_mapping, num_blocks, block_size, duplicates=True) -> dict:
+    """Violations of kv_store's preconditions: slots inside the pool and (when
+    ``duplicates``) no slot named twice."""
+    torch = _torch()
+    _dev(slot_mapping, "slot_mapping", torch.int32, 1)
+    f = _flags(slot_mapping.device)
+    bitmap = None
+    if duplicates:
+        bitmap = torch.empty((int(num_blocks) * int(block_size) + 31) // 32, dtype=torch.int32,
+                             device=slot_mapping.device)
+    _check(lib().pkv_check_slots(_ptr(slot_mapping), slot_mapping.shape[0], int(num_blocks), int(block_size),
+                                 _ptr(bitmap), _ptr(f), _stream()))
+    return _counts(f)
+
+
+def check_cascade_inputs(block_tables, context_lens, shared_lens, group_offsets, group_seqs, max_group_size,
+                         max_shared_len, block_size) -> dict:
+    """Violations of the shared-prefix groups' preconditions (see pkv.h)."""
+    torch = _torch()
+    for t, n in ((context_lens, "context_lens"), (shared_lens, "shared_lens"), (group_offsets, "group_offsets"),
+                 (group_seqs, "group_seqs")):
+        _dev(t, n, torch.int32, 1)
+    _dev(block_tables, "block_tables", torch.int32, 2)
+    B = context_lens.shape[0]
+    f = _flags(block_tables.device)
+    seen = torch.empty(max(B, 1), dtype=torch.int32, device=block_tables.device)
+    _check(lib().pkv_check_cascade_inputs(_ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+                                          _ptr(shared_lens), _ptr(group_offsets), _ptr(group_seqs),
+                                          group_offsets.shape[0] - 1, group_seqs.shape[0], B, int(max_group_size),
+                                          int(max_shared_len), int(block_size), _ptr(seen), _ptr(f), _stream()))
+    return _counts(f)
 
 
 def paged_gather(k_cache, v_cache, block_tables, cu_seqlens_k, max_seqlen_k=None, k_out=None, v_out=None):

@@ -479,6 +479,122 @@ int pkv_paged_prefill_attn(const void* q, const void* k, const void* v, const in
   return hip_status(pkv::launch_row_attn(a, dtype, head_dim, true, s), "prefill launch");
 }
 
+// ---------------------------------------------------------------- precondition checks
+
+static_assert(pkv::kCheckLength == PKV_CHECK_LENGTH && pkv::kCheckBlockId == PKV_CHECK_BLOCK_ID &&
+                  pkv::kCheckCuSeqlens == PKV_CHECK_CU_SEQLENS && pkv::kCheckSlot == PKV_CHECK_SLOT &&
+                  pkv::kCheckDuplicateSlot == PKV_CHECK_DUPLICATE_SLOT &&
+                  pkv::kCheckSharedPrefix == PKV_CHECK_SHARED_PREFIX && pkv::kCheckGroup == PKV_CHECK_GROUP &&
+                  pkv::kCheckNumFlags == PKV_CHECK_NUM_FLAGS,
+              "check codes of the kernels and of the header differ");
+
+int pkv_check_decode_inputs(const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t max_context_len, int32_t num_seqs, int64_t num_blocks, int32_t block_size,
+                            int32_t* flags, void* stream) {
+  if (!flags) return fail(PKV_ERR_INVALID_ARG, "flags is NULL");
+  if (num_seqs < 0 || max_context_len < 0 || max_blocks_per_seq < 1 || num_blocks < 1 || block_size < 1)
+    return fail(PKV_ERR_INVALID_ARG, "negative or empty size");
+  if (num_seqs > 0 && (!block_tables || !context_lens))
+    return fail(PKV_ERR_INVALID_ARG, "null block_tables or context_lens");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int st = hip_status(pkv::launch_zero(flags, PKV_CHECK_NUM_FLAGS, s), "check launch");
+  if (st) return st;
+  pkv::CheckArgs a{};
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.max_len_k = max_context_len;
+  a.num_seqs = num_seqs;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.flags = flags;
+  return hip_status(pkv::launch_check_tables(a, s), "check launch");
+}
+
+int pkv_check_prefill_inputs(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, const int32_t* block_tables,
+                             int32_t max_blocks_per_seq, int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                             int64_t num_blocks, int32_t block_size, int32_t* flags, void* stream) {
+  if (!flags) return fail(PKV_ERR_INVALID_ARG, "flags is NULL");
+  if (num_seqs < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || num_blocks < 1 || block_size < 1 ||
+      (block_tables && max_blocks_per_seq < 1))
+    return fail(PKV_ERR_INVALID_ARG, "negative or empty size");
+  if (num_seqs > 0 && (!cu_seqlens_q || !cu_seqlens_k))
+    return fail(PKV_ERR_INVALID_ARG, "null cu_seqlens_q or cu_seqlens_k");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int st = hip_status(pkv::launch_zero(flags, PKV_CHECK_NUM_FLAGS, s), "check launch");
+  if (st) return st;
+  pkv::CheckArgs a{};
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.cu_seqlens_k = cu_seqlens_k;
+  a.max_len_q = max_seqlen_q;
+  a.max_len_k = max_seqlen_k;
+  a.num_seqs = num_seqs;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.flags = flags;
+  return hip_status(pkv::launch_check_tables(a, s), "check launch");
+}
+
+int pkv_check_slots(const int32_t* slot_mapping, int64_t num_tokens, int64_t num_blocks, int32_t block_size,
+                    uint32_t* bitmap, int32_t* flags, void* stream) {
+  if (!flags) return fail(PKV_ERR_INVALID_ARG, "flags is NULL");
+  if (num_tokens < 0 || num_blocks < 1 || block_size < 1) return fail(PKV_ERR_INVALID_ARG, "negative or empty size");
+  if (num_tokens > 0 && !slot_mapping) return fail(PKV_ERR_INVALID_ARG, "slot_mapping is NULL");
+  if (num_blocks * block_size > 0x7fffffffLL) return fail(PKV_ERR_UNSUPPORTED, "pool larger than int32 slots");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int st = hip_status(pkv::launch_zero(flags, PKV_CHECK_NUM_FLAGS, s), "check launch");
+  if (st) return st;
+  if (bitmap) {
+    st = hip_status(pkv::launch_zero(reinterpret_cast<int32_t*>(bitmap), (num_blocks * block_size + 31) / 32, s),
+                    "check launch");
+    if (st) return st;
+  }
+  pkv::CheckArgs a{};
+  a.slot_mapping = slot_mapping;
+  a.num_tokens = num_tokens;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.bitmap = bitmap;
+  a.flags = flags;
+  return hip_status(pkv::launch_check_slots(a, s), "check launch");
+}
+
+int pkv_check_cascade_inputs(const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                             const int32_t* shared_lens, const int32_t* group_offsets, const int32_t* group_seqs,
+                             int32_t num_groups, int32_t num_members, int32_t num_seqs, int32_t max_group_size,
+                             int32_t max_shared_len, int32_t block_size, int32_t* seen, int32_t* flags, void* stream) {
+  if (!flags || !seen) return fail(PKV_ERR_INVALID_ARG, "flags or seen is NULL");
+  if (num_groups < 0 || num_members < 0 || num_seqs < 0 || max_group_size < 0 || max_shared_len < 0 ||
+      max_blocks_per_seq < 1 || block_size < 1)
+    return fail(PKV_ERR_INVALID_ARG, "negative or empty size");
+  if (num_seqs > 0 && (!block_tables || !context_lens || !shared_lens))
+    return fail(PKV_ERR_INVALID_ARG, "null block_tables, context_lens or shared_lens");
+  if (num_groups > 0 && (!group_offsets || (num_members > 0 && !group_seqs)))
+    return fail(PKV_ERR_INVALID_ARG, "null group_offsets or group_seqs");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int st = hip_status(pkv::launch_zero(flags, PKV_CHECK_NUM_FLAGS, s), "check launch");
+  if (!st) st = hip_status(pkv::launch_zero(seen, num_seqs, s), "check launch");
+  if (st) return st;
+  pkv::CheckArgs a{};
+  a.block_tables = block_tables;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.block_size = block_size;
+  a.shared_lens = shared_lens;
+  a.group_offsets = group_offsets;
+  a.group_seqs = group_seqs;
+  a.num_groups = num_groups;
+  a.num_members = num_members;
+  a.max_group_size = max_group_size;
+  a.max_shared_len = max_shared_len;
+  a.seen = seen;
+  a.flags = flags;
+  return hip_status(pkv::launch_check_groups(a, s), "check launch");
+}
+
 int pkv_paged_gather(const void* k_cache, const void* v_cache, const int32_t* block_tables,
                      int32_t max_blocks_per_seq, const int32_t* cu_seqlens_k, int32_t num_seqs, int32_t max_seqlen_k,
                      void* k_out, void* v_out, int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks,

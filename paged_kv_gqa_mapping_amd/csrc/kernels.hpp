@@ -114,6 +114,49 @@ struct RopeStoreArgs {
 hipError_t launch_rope_kv_store(const RopeStoreArgs& a, int32_t dtype, int32_t head_dim, bool interleaved,
                                 hipStream_t stream);
 
+// Precondition checks: counter index of each kind of violation (the same
+// numbers as pkv_check_flag in pkv.h).
+enum CheckCode : int32_t {
+  kCheckLength = 0,
+  kCheckBlockId = 1,
+  kCheckCuSeqlens = 2,
+  kCheckSlot = 3,
+  kCheckDuplicateSlot = 4,
+  kCheckSharedPrefix = 5,
+  kCheckGroup = 6,
+  kCheckNumFlags = 8,
+};
+
+struct CheckArgs {
+  const int32_t* block_tables;  // NULL: no table (packed prefill)
+  int32_t max_blocks_per_seq;
+  const int32_t* context_lens;  // decode and groups; NULL for prefill
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  int32_t max_len_q;
+  int32_t max_len_k;
+  int32_t num_seqs;
+  int64_t num_blocks;
+  int32_t block_size;
+  const int32_t* slot_mapping;
+  int64_t num_tokens;
+  uint32_t* bitmap;  // one bit per slot, or NULL (no duplicate check)
+  const int32_t* shared_lens;
+  const int32_t* group_offsets;
+  const int32_t* group_seqs;
+  int32_t num_groups;
+  int32_t num_members;  // entries of group_seqs
+  int32_t max_group_size;
+  int32_t max_shared_len;
+  int32_t* seen;   // [num_seqs] groups naming each sequence
+  int32_t* flags;  // [kCheckNumFlags]
+};
+
+hipError_t launch_zero(int32_t* p, int64_t n, hipStream_t stream);
+hipError_t launch_check_tables(const CheckArgs& a, hipStream_t stream);
+hipError_t launch_check_slots(const CheckArgs& a, hipStream_t stream);
+hipError_t launch_check_groups(const CheckArgs& a, hipStream_t stream);
+
 // Row-attention instantiation exists for this shape?
 bool row_attn_supported(int32_t dtype, int32_t head_dim, int32_t num_q_heads, int32_t num_kv_heads);
 

@@ -163,3 +163,25 @@ def test_cascade_workspace_bytes():
     # 2 member tiles x 8 head groups x chunks > 512 workgroups: 512 keys -> 32 chunks)
     got = L.pkv_cascade_workspace_bytes(64, 32, 8, 128, 16896, 512, 256, 1, 64, 16384)
     assert got == 64 * 32 * (2 + 32) * (128 + 2) * 4
+
+
+@needs_lib
+def test_check_calls_reject_bad_arguments_on_the_host():
+    L = pkv.lib()
+    p = 1 << 20
+    assert L.pkv_check_decode_inputs(p, 4, p, 100, 2, 10, 16, None, None) == -1          # no flags
+    assert L.pkv_check_decode_inputs(p, 0, p, 100, 2, 10, 16, p, None) == -1             # empty table row
+    assert L.pkv_check_decode_inputs(None, 4, p, 100, 2, 10, 16, p, None) == -1
+    assert L.pkv_check_prefill_inputs(None, p, None, 0, 2, 10, 10, 10, 16, p, None) == -1
+    assert L.pkv_check_slots(p, -1, 10, 16, None, p, None) == -1
+    assert L.pkv_check_slots(p, 5, 1 << 30, 1 << 10, None, p, None) == -2                # more slots than int32
+    assert L.pkv_check_cascade_inputs(p, 4, p, p, p, p, 1, 3, 2, 3, 64, 16, None, p, None) == -1  # no seen
+    assert L.pkv_check_cascade_inputs(p, 4, p, p, None, p, 1, 3, 2, 3, 64, 16, p, p, None) == -1
+
+
+def test_check_names_follow_the_header():
+    text = open(HEADER).read()
+    codes = dict((m.group(1).lower(), int(m.group(2)))
+                 for m in re.finditer(r"PKV_CHECK_([A-Z_]+)\s*=\s*(\d+)", text))
+    assert codes.pop("num_flags") == 8
+    assert [codes[n] for n in pkv.CHECK_NAMES] == list(range(len(pkv.CHECK_NAMES)))
