@@ -27,18 +27,33 @@ MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_traffic.md")
 
 
-DECODE_SOURCES = ("api.cpp", "common.hpp", "kernels.hpp", "row_attn.hip", "row_attn.hpp")
+# What the decode split pass is built and launched from: its kernel sources whole,
+# the argument struct, and the host functions that size its grid and workspace.
+DECODE_FILES = ("common.hpp", "row_attn.hip", "row_attn.hpp")
+DECODE_PARTS = (("kernels.hpp", "struct RowAttnArgs {"), ("api.cpp", "int32_t auto_split("),
+                ("api.cpp", "int64_t state_bytes("), ("api.cpp", "int prepare_decode("))
+
+
+def _block(text: str, start: str) -> str:
+    """The text from the line holding `start` to the first line that closes it at column 0."""
+    i = text.index(start)
+    i = text.rindex("\n", 0, i) + 1
+    j = text.index("\n}", i)
+    return text[i:text.index("\n", j + 1) + 1]
 
 
 def kernel_source_hash() -> str:
-    """sha256 over the sources the decode split pass is built from (name + bytes, in order)."""
+    """sha256 over what defines the decode split pass (file names and bytes, in order)."""
     import hashlib
 
     h = hashlib.sha256()
     d = os.path.join(ROOT, "paged_kv_gqa_mapping_amd", "csrc")
-    for name in DECODE_SOURCES:
+    for name in DECODE_FILES:
         h.update(name.encode())
         h.update(open(os.path.join(d, name), "rb").read())
+    for name, start in DECODE_PARTS:
+        h.update(f"{name}:{start}".encode())
+        h.update(_block(open(os.path.join(d, name)).read(), start).encode())
     return h.hexdigest()
 
 
