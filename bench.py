@@ -179,6 +179,8 @@ def main():
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the separately timed next-row measurements (fused rope + kv_store, cascade decode)")
+    ap.add_argument("--fused-store", action="store_true",
+                    help="write the decode tokens' K/V inside the decode launch (kv_store then covers prefill tokens only)")
     ap.add_argument("--cascade", action="store_true",
                     help="decode with shared-prefix (cascade) decode inside the step instead of plain split-K decode")
     ap.add_argument("--graph", action="store_true",
@@ -248,13 +250,20 @@ def main():
     torch.cuda.synchronize()
     log("inputs resident on the GPU")
 
+    n_pre_tok = int(w.cu_seqlens_q[-1]) if has_pre else 0  # the chunk tokens come first in slot_mapping
+    if args.fused_store and (not has_dec or args.cascade):
+        print("--fused-store needs decode sequences and plain decode", file=sys.stderr)
+        sys.exit(2)
     n_ev = 5
     def step(events=None):
         def rec(i):
             if events is not None:
                 events[i].record()
         rec(0)
-        pkv.kv_store(nk, nv, kc, vc, slots)
+        if not args.fused_store:
+            pkv.kv_store(nk, nv, kc, vc, slots)
+        elif n_pre_tok:
+            pkv.kv_store(nk[:n_pre_tok], nv[:n_pre_tok], kc, vc, slots[:n_pre_tok])
         rec(1)
         if has_pre:
             pkv.paged_prefill_attn(pq, kc, vc, cuq, cuk, pbt, pout, max_seqlen_q=w.max_seqlen_q,
@@ -262,6 +271,10 @@ def main():
         rec(2)
         if has_dec and args.cascade:
             cascade_decode(dout)
+            rec(3)
+        elif has_dec and args.fused_store:
+            pkv.paged_decode_store_attn(dq, nk[n_pre_tok:], nv[n_pre_tok:], kc, vc, dbt, dcl, w.scale, dout,
+                                        max_context_len=w.max_context_len, split_tokens=split, workspace=ws)
             rec(3)
         elif has_dec:
             pkv.paged_decode_split(dq, kc, vc, dbt, dcl, w.scale, dout, max_context_len=w.max_context_len,
@@ -312,14 +325,15 @@ def main():
     kv_bytes = w.decode_kv_bytes()
     dec_io = w.decode_io_bytes()
     flops = w.prefill_flops()
-    store_bytes = w.store_bytes()
+    stored_tokens = n_pre_tok if args.fused_store else int(len(w.slot_mapping))
+    store_bytes = w.store_bytes() * stored_tokens // max(len(w.slot_mapping), 1)
     # with --cascade the timed decode is the whole shared-prefix call, which reads the unique bytes
     split_bytes = (w.decode_kv_bytes_unique() if args.cascade else kv_bytes) + dec_io
     achieved_gbs = split_bytes / (t_split * 1e-3) / 1e9 if has_dec else 0.0
 
     kernels = {
-        "kv_store": {"ms": round(t_store, 5), "GB/s": round(store_bytes / (t_store * 1e-3) / 1e9, 1),
-                     "tokens": int(len(w.slot_mapping))},
+        "kv_store": {"ms": round(t_store, 5), "GB/s": round(store_bytes / (t_store * 1e-3) / 1e9, 1) if t_store else None,
+                     "tokens": stored_tokens},
         "decode_split": {"ms": round(t_split, 5), "GB/s": round(achieved_gbs, 1),
                          "frac_hbm": round(achieved_gbs / HBM_PEAK_GBS, 4),
                          "split_tokens": (None if args.cascade else int(split)) if has_dec else 0},

@@ -188,6 +188,32 @@ int pkv_paged_decode_reduce(const void* q, const void* k_cache, const void* v_ca
                             int32_t split_tokens, void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * Decode with the cache write fused in: the same as pkv_kv_store of each
+ * sequence's newest token followed by pkv_paged_decode_attn, in the decode
+ * launch (one launch fewer per step; the pages capture the decode step in a
+ * CUDA graph to cut launch costs, "Nano-vLLM Architecture and Performance",
+ * section "Key Features", item "CUDA Graph Capture").
+ *
+ *   k, v     [num_seqs, num_kv_heads, head_dim]: the K/V rows of each
+ *            sequence's newest token, the one at position context_lens[b] - 1
+ *            (context_lens counts it).  It is written to that position's row
+ *            of the caches: block block_tables[b][(L - 1) / block_size], row
+ *            (L - 1) % block_size.  A sequence with context_lens[b] == 0 has
+ *            no new token (nothing is written, its output is zeros).
+ *   other arguments as pkv_paged_decode_attn; the caches are written.
+ * The decode wave that owns the newest token reads it from k, v instead of
+ * the cache and writes it, so results and caches are bit-identical to the
+ * two separate calls.  That row must be private to the sequence (never a
+ * shared prefix block).
+ */
+int pkv_paged_decode_store_attn(const void* q, const void* k, const void* v, void* k_cache, void* v_cache,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                int32_t max_context_len, float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, int32_t block_size,
+                                int32_t dtype, int32_t split_tokens, void* workspace, int64_t workspace_bytes,
+                                void* stream);
+
+/*
  * Shared-prefix ("cascade") decode: the same result as pkv_paged_decode_attn
  * (up to rounding), for a batch in which groups of sequences begin with the
  * same cached blocks (prefix caching: blocks of a common prefix are reused

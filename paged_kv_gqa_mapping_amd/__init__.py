@@ -39,6 +39,7 @@ __all__ = [
     "paged_gather",
     "rope_kv_store",
     "cascade_decode_attn",
+    "paged_decode_store_attn",
     "cascade_workspace_bytes",
     "check_decode_inputs",
     "check_prefill_inputs",
@@ -92,6 +93,9 @@ def lib() -> ctypes.CDLL:
     L.pkv_kv_store.restype = ctypes.c_int
     L.pkv_rope_kv_store.argtypes = [P, P, P, P, P, P, P, I64, I32, I32, I32, I64, I32, ctypes.c_double, I32, I32, V]
     L.pkv_rope_kv_store.restype = ctypes.c_int
+    L.pkv_paged_decode_store_attn.argtypes = [P, P, P, P, P, P, I32, P, I32, F, P, I32, I32, I32, I32, I64, I32, I32,
+                                              I32, P, I64, V]
+    L.pkv_paged_decode_store_attn.restype = ctypes.c_int
     L.pkv_cascade_decode_attn.argtypes = [P, P, P, P, I32, P, I32, P, P, P, I32, I32, I32, I32, F, P, I32, I32, I32,
                                           I32, I64, I32, I32, I32, P, I64, V]
     L.pkv_cascade_decode_attn.restype = ctypes.c_int
@@ -240,7 +244,7 @@ def decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, spl
 
 
 def _decode(fn_name, q, k_cache, v_cache, block_tables, context_lens, scale, out, max_context_len, split_tokens,
-            workspace):
+            workspace, new_kv=None):
     torch = _torch()
     _dev(q, "q", ndim=3)
     _dev(k_cache, "k_cache", q.dtype, 4)
@@ -264,8 +268,9 @@ def _decode(fn_name, q, k_cache, v_cache, block_tables, context_lens, scale, out
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if DEBUG_CHECKS:
         _require(check_decode_inputs(block_tables, context_lens, max_context_len, NB, bs), fn_name)
+    head = (_ptr(q),) if new_kv is None else (_ptr(q), _ptr(new_kv[0]), _ptr(new_kv[1]))
     _check(getattr(lib(), fn_name)(
-        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        *head, _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
         int(max_context_len), float(scale), _ptr(out), B, Hq, Hkv, D, NB, bs, code, split, _ptr(workspace), ws_bytes,
         _stream()))
     return out
@@ -290,6 +295,19 @@ def paged_decode_reduce(q, k_cache, v_cache, block_tables, context_lens, scale, 
     """Second pass of paged_decode_attn (merge of the split states); same arguments and workspace as the first."""
     return _decode("pkv_paged_decode_reduce", q, k_cache, v_cache, block_tables, context_lens, scale, out,
                    max_context_len, split_tokens, workspace)
+
+
+def paged_decode_store_attn(q, k, v, k_cache, v_cache, block_tables, context_lens, scale, out, max_context_len=None,
+                            split_tokens=0, workspace=None):
+    """kv_store of each sequence's newest token (k, v [B, Hkv, D], at position
+    context_lens[b] - 1) fused into paged_decode_attn: one launch fewer, same bits."""
+    torch = _torch()
+    _dev(k, "k", q.dtype, 3)
+    _dev(v, "v", q.dtype, 3)
+    if k.shape != (q.shape[0], k_cache.shape[2], q.shape[2]) or v.shape != k.shape:
+        raise ValueError("k and v must be [num_seqs, num_kv_heads, head_dim]")
+    return _decode("pkv_paged_decode_store_attn", q, k_cache, v_cache, block_tables, context_lens, scale, out,
+                   max_context_len, split_tokens, workspace, new_kv=(k, v))
 
 
 def cascade_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len, max_own_len,

@@ -345,6 +345,27 @@ int pkv_paged_decode_attn(PKV_DECODE_ARGS) {
   return hip_status(pkv::launch_decode_reduce(call.args, call.dtype, call.head_dim, s), "decode reduce launch");
 }
 
+int pkv_paged_decode_store_attn(const void* q, const void* k, const void* v, void* k_cache, void* v_cache,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                int32_t max_context_len, float scale, void* out, int32_t num_seqs, int32_t num_q_heads,
+                                int32_t num_kv_heads, int32_t head_dim, int64_t num_blocks, int32_t block_size,
+                                int32_t dtype, int32_t split_tokens, void* workspace, int64_t workspace_bytes,
+                                void* stream) {
+  DecodeCall call;
+  int st = prepare_decode(call, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, max_context_len,
+                          scale, out, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, dtype,
+                          split_tokens, workspace, workspace_bytes);
+  if (st || call.empty) return st;
+  if (!k || !v) return fail(PKV_ERR_INVALID_ARG, "null k or v (the new tokens)");
+  if (!aligned16(k) || !aligned16(v)) return fail(PKV_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+  call.args.k_new = k;
+  call.args.v_new = v;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(pkv::launch_row_attn(call.args, call.dtype, call.head_dim, false, s), "decode split launch");
+  if (st || call.args.num_splits <= 1) return st;
+  return hip_status(pkv::launch_decode_reduce(call.args, call.dtype, call.head_dim, s), "decode reduce launch");
+}
+
 int pkv_cascade_decode_attn(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
                             int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
                             const int32_t* shared_lens, const int32_t* group_offsets, const int32_t* group_seqs,

@@ -32,6 +32,11 @@ struct RowAttnArgs {
   // attended by the group pass, which leaves ceil(kv_start[b] / prefix_chunk)
   // states at slots num_splits .. of the pair; the split pass covers the rest.
   const int32_t* kv_start;  // [B] or NULL (no shared prefixes)
+  // Decode with the store fused in: sequence b's newest token (position
+  // context_lens[b] - 1) is read from k_new/v_new [B, Hkv, D] instead of the
+  // cache, and written to its cache row by the wave that reads it.
+  const void* k_new;  // NULL: plain decode
+  const void* v_new;
   int32_t ws_stride;        // state slots per (sequence, query head): num_splits + prefix chunks
   int32_t prefix_chunk;     // keys per group-pass state
   float scale_log2;  // scale * log2(e)

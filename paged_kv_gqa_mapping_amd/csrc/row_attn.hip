@@ -50,7 +50,12 @@ hipError_t launch_one(const RowAttnArgs& a, hipStream_t stream) {
   const int64_t blocks = (int64_t)n_hg * a.num_seqs * rows;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((row_attn_kernel<BF16, D, HPW, G, U, PKV_ROW_R, PREFILL>), dim3((unsigned)blocks), dim3(64), 0, stream, a);
+  if (!PREFILL && a.k_new)
+    hipLaunchKernelGGL((row_attn_kernel<BF16, D, HPW, G, U, PKV_ROW_R, PREFILL, !PREFILL>), dim3((unsigned)blocks),
+                       dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((row_attn_kernel<BF16, D, HPW, G, U, PKV_ROW_R, PREFILL, false>), dim3((unsigned)blocks),
+                       dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

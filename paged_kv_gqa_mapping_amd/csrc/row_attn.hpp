@@ -71,7 +71,8 @@ __device__ __forceinline__ void store_words(char* p, const uint32_t* w) {
   *reinterpret_cast<T*>(p) = x;
 }
 
-template <bool BF16, int D, int HPW, int G, int U, int R, bool PREFILL>
+// STORE: decode with the newest token's cache write fused in (k_new / v_new).
+template <bool BF16, int D, int HPW, int G, int U, int R, bool PREFILL, bool STORE>
 __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
   constexpr int ELT = BF16 ? 2 : 4;
   constexpr int TL = 64 / HPW;
@@ -102,6 +103,8 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
   // This wave's query row, its key range [t0, t1), and the split index.
   int64_t q_row;
   int t0, t1, split = 0, nsplit_b = 1, k0 = 0;
+  int t_new = -1;  // fused store: position of the newest token if this wave's range holds it
+  int t_fin = -1;  // fused store: first token of the step that holds it
   if constexpr (PREFILL) {
     const int qb = a.cu_seqlens_q[b];
     const int lq = a.cu_seqlens_q[b + 1] - qb;
@@ -131,6 +134,13 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
     }
     if (t0 >= L) return;
     t1 = min(L, t0 + a.split_tokens);
+    if (STORE && t1 == L) {
+      // the step holding the newest token is taken out of the streaming loop
+      // and done after it, with that token read from k_new / v_new
+      t_new = L - 1;
+      t_fin = t0 + (t_new - t0) / U * U;
+      t1 = t_fin;
+    }
     // states merged for this row: its splits, plus the group pass's when it has a prefix
     nsplit_b = (L - start + a.split_tokens - 1) / a.split_tokens + (start > 0 ? 1 : 0);
   }
@@ -317,6 +327,40 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
       if (s >= nsteps) break;
       if (s + R - 1 < nsteps) load(ring[(r + R - 1) % R], t0 + (s + R - 1) * U);
       compute(ring[r], t0 + s * U);
+    }
+  }
+
+  if constexpr (STORE && !PREFILL) {
+    // fused store: the last step, with the same token boundaries as when
+    // streamed, so the result has the same bits as storing first; its older
+    // tokens come from the cache, the newest token and its past-the-end copies
+    // from k_new / v_new, and the newest token is written to its cache row
+    if (t_new >= 0) {
+      t1 = t_new + 1;
+      Buf fb;
+      load(fb, t_fin);
+      const int un = t_new - t_fin;
+      uint32_t nk[NW], nv[NW];
+      const char* kn = (const char*)a.k_new + (int64_t)b * row_bytes + lane_off;
+      const char* vn = (const char*)a.v_new + (int64_t)b * row_bytes + lane_off;
+      for (int jj = 0; jj < NCH; ++jj) {
+        load_words<CH>(&nk[jj * WPC], kn + jj * TL * CH);
+        load_words<CH>(&nv[jj * WPC], vn + jj * TL * CH);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (u >= un)
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            fb.k[u][w] = nk[w];
+            fb.v[u][w] = nv[w];
+          }
+      const int64_t r = step_row(t_new);
+      for (int jj = 0; jj < NCH; ++jj) {
+        store_words<CH>((char*)a.k + r * row_bytes + lane_off + jj * TL * CH, &nk[jj * WPC]);
+        store_words<CH>((char*)a.v + r * row_bytes + lane_off + jj * TL * CH, &nv[jj * WPC]);
+      }
+      compute(fb, t_fin);
     }
   }
 

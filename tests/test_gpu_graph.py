@@ -99,3 +99,46 @@ def test_graph_replay_sees_new_inputs():
         dec()
         torch.cuda.synchronize()
         assert np.array_equal(got, to_host(out, "bf16"))
+
+
+def test_graph_fused_store_decode_step_matches_eager():
+    """The decode step with the cache write fused in (one launch plus the merge)
+    captured and replayed: outputs and caches equal the eager two-call step."""
+    seqs = [W.SeqSpec("decode", L, 1) for L in (1, 17, 256, 257, 1000, 4000)]
+    w = W.build("graph-fused", 23, "bf16", 32, 8, 128, 16, seqs)
+    ref = DeviceStep(w)
+    ref.store()
+    ref.decode(split_tokens=512)
+    torch.cuda.synchronize()
+    st = DeviceStep(w)
+    B, Hq, D = st.dec_q.shape
+    ws = torch.empty(max(pkv.decode_workspace_bytes(B, Hq, D, w.max_context_len, 512), 16), dtype=torch.uint8,
+                     device="cuda")
+    k0, v0 = st.k_cache.clone(), st.v_cache.clone()
+    out = torch.empty_like(st.dec_q)
+
+    def step():
+        pkv.paged_decode_store_attn(st.dec_q, st.new_k, st.new_v, st.k_cache, st.v_cache, st.dec_bt, st.dec_cl,
+                                    w.scale, out, max_context_len=w.max_context_len, split_tokens=512, workspace=ws)
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for r in range(3):
+        out.fill_(5.0)
+        st.k_cache.copy_(k0)
+        st.v_cache.copy_(v0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        log(f"fused replay {r}")
+        assert torch.equal(out.view(torch.int16), ref.dec_out.view(torch.int16))
+        assert torch.equal(st.k_cache.view(torch.int16), ref.k_cache.view(torch.int16))
+        assert torch.equal(st.v_cache.view(torch.int16), ref.v_cache.view(torch.int16))
