@@ -17,7 +17,7 @@
 #define PKV_ROW_U 0
 #endif
 #ifndef PKV_ROW_R
-#define PKV_ROW_R 3
+#define PKV_ROW_R 2
 #endif
 
 namespace pkv {
