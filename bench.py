@@ -169,6 +169,120 @@ def measure_cascade(w, torch, cascade_decode, out, plain_ms, iters=20):
             "note": "next-row path (group pass + split pass + merge), timed separately after the step"}
 
 
+def report(iters: int = 7) -> None:
+    """Per-workload figures (workloads 1-5): median kernel times after a 1 GiB read that evicts
+    the caches, throughput against the roofline, max-abs error of sampled outputs against the
+    oracle, the stored rows bit for bit, and the oracle's own speed on those samples.  One JSON
+    line per workload."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    import paged_kv_gqa_mapping_amd as pkv
+    import workloads as W
+
+    torch.cuda.set_device(0)
+    pkv.lib()
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+
+    def dev(a, bf):
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16) if bf else \
+            torch.from_numpy(np.ascontiguousarray(a))
+        return t.cuda()
+
+    def timed(fn):
+        fn()
+        ts = []
+        for _ in range(iters):
+            flush.sum()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    for i in range(1, 6):
+        w = W.make_config(i)
+        bf = w.dtype == W.BF16
+        kc, vc = dev(w.k_cache, bf), dev(w.v_cache, bf)
+        nk, nv, slots = dev(w.new_k, bf), dev(w.new_v, bf), dev(w.slot_mapping, False)
+        rec = {"workload": w.name, "dtype": w.dtype}
+        t_store = timed(lambda: pkv.kv_store(nk, nv, kc, vc, slots))
+        rec["kv_store_us"] = round(t_store * 1e3, 2)
+        rec["kv_store_GB/s"] = round(w.store_bytes() / (t_store * 1e-3) / 1e9, 1)
+        # the stored rows, bit for bit
+        hkv, d = w.num_kv_heads, w.head_dim
+        rows = kc.view(-1, hkv, d)[slots.long()]
+        rec["kv_store_bitwise"] = bool(torch.equal(rows.view(torch.int16) if bf else rows.view(torch.int32),
+                                                   nk.view(torch.int16) if bf else nk.view(torch.int32)))
+        # host caches after the store (in place: the workload is not used again)
+        for cache, new in ((w.k_cache, w.new_k), (w.v_cache, w.new_v)):
+            cache.reshape(-1, hkv, d)[w.slot_mapping] = new
+        if w.dec_q is not None:
+            dq, dbt, dcl = dev(w.dec_q, bf), dev(w.dec_block_tables, False), dev(w.dec_context_lens, False)
+            out = torch.empty_like(dq)
+            B, Hq, _ = dq.shape
+            split = pkv.decode_split_tokens(B, Hq, hkv, d, w.max_context_len, w.block_size, 1 if bf else 0)
+            ws = torch.empty(max(pkv.decode_workspace_bytes(B, Hq, d, w.max_context_len, split), 16),
+                             dtype=torch.uint8, device="cuda")
+            t_dec = timed(lambda: pkv.paged_decode_attn(dq, kc, vc, dbt, dcl, w.scale, out,
+                                                        max_context_len=w.max_context_len, split_tokens=split,
+                                                        workspace=ws))
+            byts = w.decode_kv_bytes() + w.decode_io_bytes()
+            rec["decode_us"] = round(t_dec * 1e3, 2)
+            rec["decode_GB/s"] = round(byts / (t_dec * 1e-3) / 1e9, 1)
+            rec["decode_frac_hbm"] = round(byts / (t_dec * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+            rec["split_tokens"] = int(split)
+            lens = w.dec_context_lens
+            pick = sorted(set(int(x) for x in np.linspace(0, len(lens) - 1, 6).round()) |
+                          {int(np.argmax(lens)), int(np.argmin(lens))})
+            got = out.cpu().view(torch.int16).numpy().view(np.uint16) if bf else out.cpu().numpy()
+            t0 = time.perf_counter()
+            ref = oracle.decode(w.dec_q[pick], w.k_cache, w.v_cache, w.dec_block_tables[pick], lens[pick], w.scale,
+                                w.dtype, w.block_size)
+            t_or = time.perf_counter() - t0
+            rec["decode_max_abs_err"] = float(np.max(np.abs(W.to_float32(got[pick], w.dtype) - ref)))
+            rec["decode_rows_checked"] = len(pick)
+            sample_bytes = int(lens[pick].astype(np.int64).sum()) * 2 * hkv * d * w.elt_bytes
+            rec["oracle_decode_GB/s"] = round(sample_bytes / t_or / 1e9, 4)
+        if w.pre_q is not None:
+            pq = dev(w.pre_q, bf)
+            pbt, cuq, cuk = dev(w.pre_block_tables, False), dev(w.cu_seqlens_q, False), dev(w.cu_seqlens_k, False)
+            pout = torch.empty_like(pq)
+            t_pre = timed(lambda: pkv.paged_prefill_attn(pq, kc, vc, cuq, cuk, pbt, pout, max_seqlen_q=w.max_seqlen_q,
+                                                         max_seqlen_k=w.max_seqlen_k, scale=w.scale))
+            fl = w.prefill_flops()
+            rec["prefill_us"] = round(t_pre * 1e3, 2)
+            rec["prefill_TFLOP/s"] = round(fl / (t_pre * 1e-3) / 1e12, 1)
+            rec["prefill_frac_mfma"] = round(fl / (t_pre * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFS, 4)
+            got = pout.cpu().view(torch.int16).numpy().view(np.uint16)
+            worst, n_rows, t_or, pairs = 0.0, 0, 0.0, 0
+            for sq in range(len(w.cu_seqlens_q) - 1):
+                q0, q1 = int(w.cu_seqlens_q[sq]), int(w.cu_seqlens_q[sq + 1])
+                lk = int(w.cu_seqlens_k[sq + 1] - w.cu_seqlens_k[sq])
+                for r in sorted({0, (q1 - q0) // 2, q1 - q0 - 1}):
+                    p_ = lk - (q1 - q0) + r
+                    t0 = time.perf_counter()
+                    ref = oracle.decode(w.pre_q[q0 + r:q0 + r + 1], w.k_cache, w.v_cache,
+                                        w.pre_block_tables[sq:sq + 1], np.array([p_ + 1], np.int32), w.scale,
+                                        w.dtype, w.block_size)
+                    t_or += time.perf_counter() - t0
+                    pairs += p_ + 1
+                    worst = max(worst, float(np.max(np.abs(W.to_float32(got[q0 + r], w.dtype) - ref[0]))))
+                    n_rows += 1
+            rec["prefill_max_abs_err"] = worst
+            rec["prefill_rows_checked"] = n_rows
+            rec["oracle_prefill_TFLOP/s"] = round(4 * w.num_q_heads * d * pairs / t_or / 1e12, 6)
+        rec["oracle_cores"] = int(threads)
+        print(json.dumps(rec), flush=True)
+        del kc, vc
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +299,8 @@ def main():
                     help="decode with shared-prefix (cascade) decode inside the step instead of plain split-K decode")
     ap.add_argument("--graph", action="store_true",
                     help="capture the step in a HIP graph and time graph replays (per-kernel events are not recorded)")
+    ap.add_argument("--report", action="store_true",
+                    help="per-workload figures of workloads 1-5 (one JSON line each) instead of the step benchmark")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -203,6 +319,9 @@ def main():
     torch.cuda.set_device(0)
     if args.calibrate_copy:
         calibrate_copy(args.calibrate_copy)
+        return
+    if args.report:
+        report()
         return
     pkv.lib()  # fail loudly if the library is missing
 
