@@ -77,7 +77,8 @@ __global__ __launch_bounds__(256, NBW == 1 ? 2 : 1) void prefill_mfma_kernel(Pre
   __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][D * VS];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // wave-uniform (scalar): the tile loop bounds and the block-id lookups derive from it
+  const int wave = uniform(tid >> 6);
   const int lane = tid & 63;
   const int col = lane & 31;
   const int half = lane >> 5;
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(256, NBW == 1 ? 2 : 1) void prefill_mfma_kernel(Pre
   const uint16_t* vbase = (const uint16_t*)a.v;
   const int k_row = (tid & 15) + 16 * (tid >> 6);
   const int k_c0 = (tid >> 4) & 3;
-  const bool v_loader = uniform(wave) < VT / 64;  // whole waves (VT is a multiple of 64)
+  const bool v_loader = wave < VT / 64;  // whole waves (VT is a multiple of 64)
   const int v_kg = tid & 15;
   const int v_dc = tid >> 4;
 
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(256, NBW == 1 ? 2 : 1) void prefill_mfma_kernel(Pre
   // block id holding key t (relative to key_base; packed K/V: unused)
   auto block_id = [&](int t) -> int32_t { return table ? table[(key_base + min(t, last_key)) >> lbs] : 0; };
   // UT: block id of the tile starting at key t (t <= last_key), the same for every lane
-  auto tile_block = [&](int t) -> int32_t { return table ? uniform(table[(key_base + t) >> lbs]) : 0; };
+  auto tile_block = [&](int t) -> int32_t { return table ? table[uniform((key_base + t) >> lbs)] : 0; };
   // element offset of key tc's row (tc <= last_key) for KV head g; blk is the block holding tc
   const int row_stride = Hkv * D;
   const int64_t blk_stride = (int64_t)row_stride << lbs;
@@ -401,16 +402,20 @@ __global__ __launch_bounds__(256, NBW == 1 ? 2 : 1) void prefill_mfma_kernel(Pre
   write_lds(PKV_S0, 0);
   __syncthreads();
   if (n_kt > 2) {
-    issue_loads(PKV_S0, 2, bk, bv);
+    const int32_t ck = bk, cv = bv;
     if (n_kt > 3) next_ids(3);
+    issue_loads(PKV_S0, 2, ck, cv);
   }
   // tile kt: compute it, move tile kt+1 from its stage `wr` to LDS, refill `wr` with tile kt+3
   auto step = [&](int kt, PKV_STAGE_PARAMS, bool with_compute) {
     if (with_compute) compute(kt & 1, kt * kKT);
     if (kt + 1 < n_kt) write_lds(k0r, k1r, k2r, k3r, v0, v1, v2, v3, (kt & 1) ^ 1);
     if (kt + 3 < n_kt) {
-      issue_loads(k0r, k1r, k2r, k3r, v0, v1, v2, v3, kt + 3, bk, bv);
+      // the next tile's block ids are requested before this tile's rows, so that
+      // waiting for them later never waits for these rows (loads retire in order)
+      const int32_t ck = bk, cv = bv;
       if (kt + 4 < n_kt) next_ids(kt + 4);
+      issue_loads(k0r, k1r, k2r, k3r, v0, v1, v2, v3, kt + 3, ck, cv);
     }
     __syncthreads();
   };
