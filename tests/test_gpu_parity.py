@@ -45,6 +45,8 @@ DECODE_SHAPES = [
     ("bf16", 16, 2, 64, 8),
     ("bf16", 64, 8, 128, 64),
     ("bf16", 4, 4, 64, 16),
+    ("bf16", 8, 2, 128, 1024),  # the largest block size the ABI takes
+    ("f32", 8, 2, 64, 8),       # the smallest
 ]
 
 
@@ -74,6 +76,8 @@ PREFILL_SHAPES = [
     ("bf16", 8, 4, 64, 256),
     ("f32", 8, 2, 64, 16),
     ("f32", 32, 8, 128, 256),
+    ("bf16", 32, 8, 128, 1024),  # the largest block size the ABI takes
+    ("bf16", 16, 4, 128, 8),     # the smallest
 ]
 
 
