@@ -71,6 +71,7 @@ struct PrefillArgs {
   int32_t max_blocks_per_seq;
   int32_t log2_block_size;
   int32_t max_seqlen_q;
+  int32_t tiles_per_pair;  // set by the launcher: query tiles per (sequence, head group)
   // Group pass of shared-prefix decode (q is [B, Hq, D]; NULL group_seqs = prefill):
   // group gi's members are group_seqs[group_offsets[gi] ..], all sharing their
   // first shared_lens[member] keys (same blocks); each workgroup takes up to

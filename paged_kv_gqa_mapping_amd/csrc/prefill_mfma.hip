@@ -1,25 +1,38 @@
 // Causal varlen prefill attention on the gfx950 matrix cores (bf16 operands,
 // fp32 accumulation), over paged or packed K/V.
 //
-// Work split: a workgroup (4 waves) takes one sequence, one group of HW query
-// heads that share a KV head, and QP = 32 * (4 / HW) consecutive query
-// positions; each wave owns 32 (position, head) columns.  The workgroup walks
-// the key axis in tiles of 64 keys up to its last query's position, staging
-// each K tile (row-major) and V tile (transposed) in LDS once for all 4
-// waves, i.e. once for the whole GQA head group.
+// Work split: a workgroup (4 waves, one per SIMD) takes one sequence, one group
+// of HW query heads that share a KV head, and QP = 32 * (8 / HW) consecutive
+// query positions: 8 column blocks of 32 (position, head) columns, block cb =
+// 2 * wave + nb holding head cb % HW and positions 32 * (cb / HW) .. +31 of the
+// tile.  Each wave thus multiplies every K/V operand fragment it reads from LDS
+// into two column blocks.  The workgroup walks the key axis in tiles of 64 keys
+// up to its last query's position; each K and V tile is staged in LDS once for
+// the whole GQA head group.
+//
+// Tile staging: the global -> LDS copies are direct (global_load_lds_dwordx4:
+// 64 lanes x 16 bytes per instruction), through a ring of 3 tile buffers, so
+// two tiles are in flight while one is computed and no register or VALU work
+// is spent on them.  K and V are stored row-major (one row per key, no
+// padding); the 16-byte slot that holds chunk c of key row k is rotated by
+// the key (K: (c + k) mod D/8; V: (c + 2 (k mod 4)) mod D/8), which keeps the
+// fragment reads below free of bank conflicts.
 //
 // Per tile and wave, with v_mfma_f32_32x32x16_bf16:
-//   S^T[key][col] = K_tile * Q^T     (2 key blocks x D/16 steps)
+//   S^T[key][col] = K_tile * Q^T     (2 key blocks x D/16 steps, ds_read_b128)
 //   online softmax per column: the accumulator gives each lane one column and
 //   16 keys per key block, so the row max and sum are in-lane plus one
 //   half-wave exchange;
 //   O^T[d][col] += V^T * P^T         (D/32 blocks x 4 steps), where P^T is the
-//   S^T accumulator itself, rounded to bf16: the lane/register layout of an
-//   MFMA result is the layout of its B operand up to a fixed permutation of
-//   the 16 keys of each step, and V^T is written to LDS in that permuted key
-//   order so no data moves between lanes.
+//   S^T accumulator itself, rounded to bf16.  The lane/register layout of an
+//   MFMA result is that of its B operand up to a fixed permutation of the 16
+//   keys of each step; the V^T fragments are read with ds_read_b64_tr_b16
+//   (a transposing LDS read: in each 16-lane group, lane l receives element
+//   l % 4 of the 8-byte rows addressed by lanes l / 4 + 4 j, j = 0..3) with
+//   row addresses chosen in that permuted key order, so no data moves between
+//   lanes.
 // Query i of a sequence sits at position Lk - Lq + i and sees keys <= it; the
-// mask is applied only on tiles that reach past a wave's first position.
+// mask is applied only on tiles that reach past a column block's first position.
 //
 // SHARED mode is the group pass of shared-prefix ("cascade") decode: the
 // columns are the decode queries of the members of one group (sequences
@@ -32,49 +45,68 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
-// Column blocks of 32 (position, head) columns per wave (1 or 2); 2 reuses
-// every LDS operand fragment twice at one wave per SIMD.
-#ifndef PKV_PF_NBW
-#define PKV_PF_NBW 1
-#endif
-
-// Tiles of K/V whose global loads are in flight while a tile is computed (1 or
-// 2 register stages).
-#ifndef PKV_PF_DEPTH
-#define PKV_PF_DEPTH 2
-#endif
-
 namespace pkv {
 
 namespace {
 
-constexpr int kKT = 64;  // keys per tile
+constexpr int kKT = 64;   // keys per tile
+constexpr int kCB = 8;    // column blocks per workgroup
+constexpr int kBufs = 3;  // tile buffers in the LDS ring
+#ifndef PKV_PF_XCDS
+#define PKV_PF_XCDS 8
+#endif
+constexpr int kXcds = PKV_PF_XCDS;  // accelerator dies (XCDs), each with its own L2
 
-// Column of key k (0..63) of a tile inside a V^T row: within each group of 16
-// keys, lane half h and slot j of the MFMA B operand hold key (j/4)*8 + h*4 +
-// j%4, so key k is stored at h*8 + j.
-__device__ __forceinline__ int vt_column(int k) {
-  const int k16 = k & 15;
-  return (k & ~15) + ((k16 & 7) >> 2) * 8 + (k16 >> 3) * 4 + (k16 & 3);
+// Column blocks per wave: 1 (8 waves per workgroup, two per SIMD) or 2 (4 waves,
+// one per SIMD, every LDS fragment feeding two MFMAs).
+#ifndef PKV_PF_NB
+#define PKV_PF_NB 1
+#endif
+constexpr int kNB = PKV_PF_NB;
+constexpr int kWaves = kCB / kNB;
+constexpr int kThreads = 64 * kWaves;
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4_t lds_short4_t;
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+// Read-only global data seen through the constant address space: uniform
+// loads from it are scalar loads (lgkmcnt), which never wait for the vmcnt-
+// counted tile copies.
+typedef const __attribute__((address_space(4))) int32_t const_i32_t;
+
+// LDS byte address of a shared-memory pointer (the low word of its flat address).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_u8_t*)p;
 }
 
-// UT: every 64-key tile lies in one block (block_size >= 64, or packed K/V), so
-// a tile's base address is the same for the whole wave and only the row within
-// the tile is per lane.
-template <int D, int HW, int NBW, bool SHARED, bool UT>
-__global__ __launch_bounds__(256, NBW == 1 ? 2 : 1) void prefill_mfma_kernel(PrefillArgs a) {
-  constexpr int PB = 4 / HW;           // position blocks (of 32 * NBW) per workgroup
-  constexpr int WP = 32 * NBW;         // positions per wave
-  constexpr int QP = WP * PB;          // positions per workgroup
+// One direct global -> LDS copy: lane i's 16 bytes at g land at LDS byte
+// m0 + 16 i.  Issued through inline asm so that the compiler does not turn it
+// into a wait for every in-flight copy before each LDS read; the waits for
+// these copies are the explicit vmcnt waits below (vector memory operations
+// retire in order).  No memory clobber: every LDS read of a tile buffer is
+// separated from the copies into that buffer by a workgroup barrier (a
+// compiler fence too), and without it the block-table reads stay scalar loads.
+__device__ __forceinline__ void copy_to_lds(const void* g, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int D, int HW, bool SHARED>
+__global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a) {
+  constexpr int QP = 32 * (kCB / HW);  // positions (members) per workgroup
   constexpr int KSTEPS = D / 16;       // contraction steps of Q K^T
   constexpr int MD = D / 32;           // 32-row blocks of O^T
-  constexpr int KS = D + 8;            // LDS K row stride (elements): 16-byte pad
-  constexpr int VS = kKT + 8;          // LDS V^T row stride (elements)
-  constexpr int CPR = D / 8;           // 16-byte chunks per K/V row
-  constexpr int CPT = CPR / 4;         // K chunks per thread (4 threads per K row)
-  constexpr int VT = (kKT / 4) * CPR;  // threads that load V (4 keys x 8 dims each)
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kKT * KS];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][D * VS];
+  constexpr int ROWB = 2 * D;          // bytes per K/V row in LDS
+  constexpr int CPR = D / 8;           // 16-byte slots per row
+  constexpr int TILEB = kKT * ROWB;    // bytes per K (or V) tile
+  constexpr int RPI = 1024 / ROWB;     // rows per copy instruction (4 or 8)
+  constexpr int RW = kKT / kWaves;     // rows of each tile copied by one wave (8 or 16)
+  constexpr int IPW = RW / RPI;        // copy instructions per wave, tile and tensor
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kBufs][2][TILEB];
 
   const int tid = threadIdx.x;
   // wave-uniform (scalar): the tile loop bounds and the block-id lookups derive from it
@@ -88,8 +120,11 @@ __global__ __launch_bounds__(256, NBW == 1 ? 2 : 1) void prefill_mfma_kernel(Pre
   const int NHG = Hq / HW;
 
   int id = blockIdx.x;
-  const int hg = id % NHG;
-  id /= NHG;
+  int hg;
+  if constexpr (SHARED) {
+    hg = id % NHG;
+    id /= NHG;
+  }
   // Prefill: sequence b, its query tile `tile` (Lq queries, Lk keys, packed
   // rows from k0).  Shared: group member tile `tile` (Lq members), keys
   // [key_base, key_base + Lk) of the prefix, table row of the group's first
@@ -109,8 +144,17 @@ __global__ __launch_bounds__(256, NBW == 1 ? 2 : 1) void prefill_mfma_kernel(Pre
     if (key_base >= shared) return;
     Lk = min(shared - key_base, a.chunk_tokens);
   } else {
-    b = id % a.num_seqs;
-    const int tile_rev = id / a.num_seqs;
+    // Workgroups are dispatched to the 8 XCDs round-robin (block B on XCD
+    // B % 8), each XCD with its own L2.  The query tiles of one (sequence, head
+    // group) pair are placed on one XCD at consecutive slots, so the workgroups
+    // that run there together read the same K/V tiles through that L2.
+    const int xcd = id % kXcds;
+    const int slot = id / kXcds;
+    const int pair = (slot / a.tiles_per_pair) * kXcds + xcd;
+    if (pair >= a.num_seqs * NHG) return;
+    const int tile_rev = slot % a.tiles_per_pair;
+    hg = pair % NHG;
+    b = pair / NHG;
     q0 = a.cu_seqlens_q[b];
     Lq = a.cu_seqlens_q[b + 1] - q0;
     k0 = a.cu_seqlens_k[b];
@@ -119,28 +163,26 @@ __global__ __launch_bounds__(256, NBW == 1 ? 2 : 1) void prefill_mfma_kernel(Pre
     tile = n_qt - 1 - tile_rev;  // tiles with the most keys are dispatched first
     if (tile < 0) return;
   }
-
-  const int hl = wave % HW;
-  const int pb = wave / HW;
-  const int h = hg * HW + hl;
   const int g = (hg * HW) / G;
   // Positions are relative to key_base.  Prefill: query i sits at shift + i.
   // Shared: every column sees the whole chunk, as a query at its last key.
   const int shift = Lk - Lq;
-  const int w_first = tile * QP + pb * WP;
-  const int w_last = min(w_first + WP, Lq) - 1;
-  const bool wave_active = w_first < Lq;
-  const int w_min_pos = SHARED ? Lk - 1 : shift + w_first;
-  const int w_max_pos = SHARED ? Lk - 1 : shift + w_last;
-  // column block nb of the wave holds queries (members) w_first + 32 nb + col
-  int pos[NBW];
-  bool col_valid[NBW];
-  int64_t q_row[NBW];  // row of q[., Hq, D] (times Hq, plus the head)
+
+  // column block nb of this wave: head h[nb], queries (members) first[nb] + col
+  int first[kNB], pos[kNB], min_pos[kNB];
+  bool col_valid[kNB];
+  int64_t q_row[kNB];  // row of q[., Hq, D] (times Hq, plus the head)
+  int w_max_pos = -1;
 #pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) {
-    const int qi = w_first + 32 * nb + col;
+  for (int nb = 0; nb < kNB; ++nb) {
+    const int cb = kNB * wave + nb;
+    const int h = hg * HW + cb % HW;
+    first[nb] = tile * QP + 32 * (cb / HW);
+    const int qi = first[nb] + col;
     col_valid[nb] = qi < Lq;
     pos[nb] = (col_valid[nb] && !SHARED) ? shift + qi : Lk - 1;
+    min_pos[nb] = SHARED ? Lk - 1 : shift + first[nb];
+    if (first[nb] < Lq) w_max_pos = max(w_max_pos, SHARED ? Lk - 1 : shift + min(first[nb] + 32, Lq) - 1);
     if constexpr (SHARED) {
       q_row[nb] = col_valid[nb] ? (int64_t)a.group_seqs[member0 + qi] * Hq + h : 0;
     } else {
@@ -149,178 +191,154 @@ __global__ __launch_bounds__(256, NBW == 1 ? 2 : 1) void prefill_mfma_kernel(Pre
   }
   const int wg_max_pos = SHARED ? Lk - 1 : shift + min(tile * QP + QP, Lq) - 1;
   const int n_kt = wg_max_pos / kKT + 1;
+  const int n_kt_wave = w_max_pos >= 0 ? min(n_kt, w_max_pos / kKT + 1) : 0;
 
-  // Q^T as the B operand: lane (col, half) holds Q[col][16 kk + 8 half .. +8].
-  bf16x8_t qf[NBW][KSTEPS];
-#pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) {
-    const uint16_t* qp = (const uint16_t*)a.q + q_row[nb] * D + 8 * half;
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (col_valid[nb]) x = *reinterpret_cast<const uint4*>(qp + 16 * kk);
-      qf[nb][kk] = __builtin_bit_cast(bf16x8_t, x);
-    }
-  }
-
-  // Tile loads.  K: thread t owns row (t % 16) + 16 (t / 64) and chunks
-  // ((t / 16) % 4) + 4 i, so 16 consecutive lanes write one chunk of 16
-  // consecutive rows (the row stride keeps them on distinct banks) and each
-  // global load instruction reads 64 contiguous bytes of 16 rows.  V: thread t
-  // owns keys 4 (t % 16) .. +3 and dims 8 (t / 16) .. +7, so 16 consecutive
-  // lanes write the 16 eight-byte key slots of one V^T row (128 contiguous
-  // bytes).
-  const int32_t* table = a.block_tables ? a.block_tables + (int64_t)b * a.max_blocks_per_seq : nullptr;
+  // Tile copies.  Wave w copies rows RW w .. RW w + RW - 1 of each K and V tile
+  // (IPW instructions each, RPI rows per instruction); lane L of an
+  // instruction fills slot L % CPR of row L / CPR.  Rows past the end of the
+  // sequence re-read the last key's row: their scores are masked (key > every
+  // position) and their weights are exactly 0, so finite data suffices.
+  const_i32_t* table =
+      a.block_tables ? (const_i32_t*)(a.block_tables + (int64_t)b * a.max_blocks_per_seq) : nullptr;
   const int lbs = a.log2_block_size;
   const int bs_mask = (1 << lbs) - 1;
-  const uint16_t* kbase = (const uint16_t*)a.k;
-  const uint16_t* vbase = (const uint16_t*)a.v;
-  const int k_row = (tid & 15) + 16 * (tid >> 6);
-  const int k_c0 = (tid >> 4) & 3;
-  const bool v_loader = wave < VT / 64;  // whole waves (VT is a multiple of 64)
-  const int v_kg = tid & 15;
-  const int v_dc = tid >> 4;
-
-  // Keys past the end of the sequence (the tail of the last tile) re-read the
-  // last key's row: their scores are masked (key > every position) and their
-  // weights are exactly 0, so finite data suffices and no zero fill is needed.
+  const uint8_t* kbytes = (const uint8_t*)a.k;
+  const uint8_t* vbytes = (const uint8_t*)a.v;
   const int last_key = Lk - 1;
-  // block id holding key t (relative to key_base; packed K/V: unused)
-  auto block_id = [&](int t) -> int32_t { return table ? table[(key_base + min(t, last_key)) >> lbs] : 0; };
-  // UT: block id of the tile starting at key t (t <= last_key), the same for every lane
-  auto tile_block = [&](int t) -> int32_t { return table ? table[uniform((key_base + t) >> lbs)] : 0; };
-  // element offset of key tc's row (tc <= last_key) for KV head g; blk is the block holding tc
-  const int row_stride = Hkv * D;
-  const int64_t blk_stride = (int64_t)row_stride << lbs;
-  const int head_off = g * D;
-  auto row_elem = [&](int tc, int32_t blk) -> int64_t {
-    if (table) return (int64_t)blk * blk_stride + (((key_base + tc) & bs_mask) * row_stride + head_off);
-    return (int64_t)(k0 + tc) * row_stride + head_off;
+  const int64_t row_bytes = (int64_t)Hkv * ROWB;
+  const int64_t blk_bytes = row_bytes << lbs;
+  const int64_t head_bytes = (int64_t)g * ROWB;
+  const int lr = lane / CPR;
+  const int ls = lane % CPR;
+  // rows RW w + 8 j .. + 7 lie in one block (block_size >= 8): its id, per group j
+  // of 8 rows (the same block for both groups of 16 rows unless block_size is 8)
+  constexpr int NBLK = RW / 8;
+  int32_t blk[NBLK];
+#pragma unroll
+  for (int j = 0; j < NBLK; ++j) blk[j] = 0;
+  auto fetch_blocks = [&](int t) {
+    if (!table) return;
+#pragma unroll
+    for (int j = 0; j < NBLK; ++j)
+      blk[j] = table[uniform((key_base + min(t * kKT + RW * wave + 8 * j, last_key)) >> lbs)];
+  };
+  // copy instruction i of tile t into buffer buf: K rows for i < IPW, then V rows
+  auto issue_copy = [&](int t, int buf, int i) {
+    const int ii = i % IPW;
+    const bool is_v = i >= IPW;
+    const int rt = RW * wave + ii * RPI + lr;  // row within the tile
+    const int tc = min(t * kKT + rt, last_key);
+    const int64_t row = table ? (int64_t)blk[(ii * RPI) / 8] * blk_bytes + (int64_t)((key_base + tc) & bs_mask) * row_bytes
+                              : (int64_t)(k0 + tc) * row_bytes;
+    const int ch = is_v ? (ls - 2 * (rt & 3)) & (CPR - 1) : (ls - rt) & (CPR - 1);
+    const uint32_t dst = lds_addr(&lds[buf][is_v ? 1 : 0][0]) + RW * wave * ROWB + ii * 1024;
+    copy_to_lds((is_v ? vbytes : kbytes) + row + head_bytes + 16 * ch, uniform(dst));
+  };
+  auto issue_copies = [&](int t, int buf) {
+#pragma unroll
+    for (int i = 0; i < 2 * IPW; ++i) issue_copy(t, buf, i);
   };
 
-  static_assert(CPT == 2 || CPT == 4, "head_dim 64 or 128");
-  // Prefetched rows of one tile (a stage): K chunks k_c0 + 4 i (i < CPT) and
-  // the V rows of keys 4 kg .. 4 kg + 3, passed as separate values so that
-  // they stay in registers.
-#define PKV_STAGE_PARAMS uint4 &k0r, uint4 &k1r, uint4 &k2r, uint4 &k3r, uint4 &v0, uint4 &v1, uint4 &v2, uint4 &v3
-  auto issue_loads = [&](PKV_STAGE_PARAMS, int kt, int32_t bk, int32_t bv) {
-    if constexpr (UT) {
-      // bk is the tile's block; rows past the end re-read the last key's row
-      const int t0 = kt * kKT;
-      const int64_t tile = table ? (int64_t)bk * blk_stride + (int64_t)((key_base + t0) & bs_mask) * row_stride
-                                 : (int64_t)(k0 + t0) * row_stride;
-      const int last = last_key - t0;
-      const uint16_t* kp = kbase + tile + (min(k_row, last) * row_stride + head_off + k_c0 * 8);
-      k0r = *reinterpret_cast<const uint4*>(kp);
-      k1r = *reinterpret_cast<const uint4*>(kp + 32);
-      if constexpr (CPT == 4) {
-        k2r = *reinterpret_cast<const uint4*>(kp + 64);
-        k3r = *reinterpret_cast<const uint4*>(kp + 96);
-      }
-      if (v_loader) {
-        const uint16_t* vp = vbase + tile + (head_off + v_dc * 8);
-        const int tv = 4 * v_kg;
-        v0 = *reinterpret_cast<const uint4*>(vp + min(tv, last) * row_stride);
-        v1 = *reinterpret_cast<const uint4*>(vp + min(tv + 1, last) * row_stride);
-        v2 = *reinterpret_cast<const uint4*>(vp + min(tv + 2, last) * row_stride);
-        v3 = *reinterpret_cast<const uint4*>(vp + min(tv + 3, last) * row_stride);
-      }
-      return;
-    }
-    const int64_t ek = row_elem(min(kt * kKT + k_row, last_key), bk) + k_c0 * 8;
-    k0r = *reinterpret_cast<const uint4*>(kbase + ek);
-    k1r = *reinterpret_cast<const uint4*>(kbase + ek + 32);
-    if constexpr (CPT == 4) {
-      k2r = *reinterpret_cast<const uint4*>(kbase + ek + 64);
-      k3r = *reinterpret_cast<const uint4*>(kbase + ek + 96);
-    }
-    if (v_loader) {
-      // the 4 keys are consecutive rows of one block (4-aligned, block_size >= 8);
-      // keys past the end all read the last key's row
-      const int tv = kt * kKT + 4 * v_kg;
-      const int tvc = min(tv, last_key);
-      const int64_t ev = row_elem(tvc, bv) + v_dc * 8;
-      auto row = [&](int i) {
-        return *reinterpret_cast<const uint4*>(vbase + ev + (int64_t)((min(tv + i, last_key) - tvc) * row_stride));
-      };
-      v0 = row(0);
-      v1 = row(1);
-      v2 = row(2);
-      v3 = row(3);
-    }
-  };
-  auto write_lds = [&](PKV_STAGE_PARAMS, int buf) {
-    uint16_t* kd = &lds_k[buf][k_row * KS + k_c0 * 8];
-    *reinterpret_cast<uint4*>(kd) = k0r;
-    *reinterpret_cast<uint4*>(kd + 32) = k1r;
-    if constexpr (CPT == 4) {
-      *reinterpret_cast<uint4*>(kd + 64) = k2r;
-      *reinterpret_cast<uint4*>(kd + 96) = k3r;
-    }
-    if (v_loader) {
-      const int vc = vt_column(4 * v_kg);
-      const uint32_t r0[4] = {v0.x, v0.y, v0.z, v0.w};
-      const uint32_t r1[4] = {v1.x, v1.y, v1.z, v1.w};
-      const uint32_t r2[4] = {v2.x, v2.y, v2.z, v2.w};
-      const uint32_t r3[4] = {v3.x, v3.y, v3.z, v3.w};
+  // Fragment read offsets within a tile buffer.
+  // K (A operand of S^T): lane (col, half), step kk: key row col (+ 32 mb, which
+  // keeps the rotation), chunk 2 kk + half.
+  uint32_t koff[KSTEPS];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int d = v_dc * 8 + 2 * w;
-        // v_perm_b32: selector bytes 0-3 pick from the second operand, 4-7 from the first
-        uint2 lo, hi;
-        lo.x = __builtin_amdgcn_perm(r1[w], r0[w], 0x05040100u);  // (key 0, key 1) of dim d
-        lo.y = __builtin_amdgcn_perm(r3[w], r2[w], 0x05040100u);  // (key 2, key 3)
-        hi.x = __builtin_amdgcn_perm(r1[w], r0[w], 0x07060302u);  // dim d + 1
-        hi.y = __builtin_amdgcn_perm(r3[w], r2[w], 0x07060302u);
-        *reinterpret_cast<uint2*>(&lds_v[buf][d * VS + vc]) = lo;
-        *reinterpret_cast<uint2*>(&lds_v[buf][(d + 1) * VS + vc]) = hi;
-      }
-    }
-  };
+  for (int kk = 0; kk < KSTEPS; ++kk) koff[kk] = col * ROWB + 16 * ((2 * kk + half + col) & (CPR - 1));
+  // V^T (A operand of O^T), transposing read: lane L = 16 grp + r supplies the
+  // 8-byte row of key 8 s + 4 half + r / 4 of a 16-key step (the MFMA's key
+  // order) at dims 32 md + 16 (grp % 2) + 4 (r % 4) .. +3, which is chunk
+  // 4 md + 2 (grp % 2) + (r % 4) / 2 at byte 8 (r % 2) of it.
+  uint32_t voff[MD];
+  {
+    const int r = lane & 15;
+    const int grp = lane >> 4;
+    const int qr = 2 * (grp & 1) + (r & 3) / 2 + 2 * (r >> 2);
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+      voff[md] = (4 * half + (r >> 2)) * ROWB + 16 * ((4 * md + qr) & (CPR - 1)) + 8 * (r & 1);
+  }
 
-  f32x16_t acc_o[NBW][MD];
+  // Q^T as the B operand: lane (col, half) holds Q[col][16 kk + 8 half .. +8].
+  bf16x8_t qf[kNB][KSTEPS];
+  f32x16_t acc_o[kNB][MD];
 #pragma unroll
-  for (int nb = 0; nb < NBW; ++nb)
+  for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc_o[nb][md][r] = 0.f;
-  float m[NBW], lsum[NBW];  // running reference max (log2 units) and this half-wave's weight sum, per column
+  float m[kNB], lsum[kNB];  // running reference max (log2 units) and this half-wave's weight sum, per column
 #pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) {
+  for (int nb = 0; nb < kNB; ++nb) {
     m[nb] = kNegInf;
     lsum[nb] = 0.f;
   }
   const float c = a.scale_log2;  // > 0
   const uint32_t kOnes = 0x3F803F80u;  // bf16 pair (1, 1)
 
+  // Scheduling groups (instruction classes of __builtin_amdgcn_sched_group_barrier).
+  constexpr int kSchedMfma = 0x008;
+  constexpr int kSchedDsRead = 0x100;
+  constexpr int kKR = 2 * KSTEPS;  // K fragment reads per tile
+  constexpr int kKPF = 4;          // K fragment reads in flight
+  constexpr int kVR = 4 * MD;      // V^T fragments per tile (two transposing reads each)
+  constexpr int kVPF = 3;          // V^T fragments in flight
+
   auto compute = [&](int buf, int key0) {
-    // S^T = K Q^T (raw scores); each K fragment feeds the NBW column blocks
-    f32x16_t acc_s[NBW][2];
+    const uint8_t* kt_lds = &lds[buf][0][0];
+    const uint8_t* vt_lds = &lds[buf][1][0];
+    // fragment i of K: step kk = i / 2, key block mb = i % 2
+    auto k_frag = [&](int i) {
+      return __builtin_bit_cast(bf16x8_t,
+                                *reinterpret_cast<const uint4*>(kt_lds + koff[i >> 1] + (i & 1) * 32 * ROWB));
+    };
+    // fragment j of V^T: key step ks = j / MD, dim block md = j % MD
+    auto v_frag = [&](int j) {
+      const uint8_t* vp = vt_lds + voff[j % MD] + (j / MD) * 16 * ROWB;
+      const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(vp));
+      const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(vp + 8 * ROWB));
+      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // S^T = K Q^T (raw scores); each K fragment feeds the kNB column blocks,
+    // and the reads run kKPF fragments ahead of the MFMAs.  The first V^T
+    // fragments are requested at the end, so that they arrive during the softmax.
+    f32x16_t acc_s[kNB][2];
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb)
+    for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc_s[nb][mb][r] = 0.f;
+    bf16x8_t kf[kKR];
+    bf16x8_t vf[kVR];
 #pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
+    for (int i = 0; i < kKPF; ++i) kf[i] = k_frag(i);
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8_t af = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const uint4*>(&lds_k[buf][(mb * 32 + col) * KS + 16 * kk + 8 * half]));
+    for (int i = 0; i < kKR; ++i) {
+      if (i + kKPF < kKR) kf[i + kKPF] = k_frag(i + kKPF);
 #pragma unroll
-        for (int nb = 0; nb < NBW; ++nb)
-          acc_s[nb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, qf[nb][kk], acc_s[nb][mb], 0, 0, 0);
-      }
+      for (int nb = 0; nb < kNB; ++nb)
+        acc_s[nb][i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[nb][i >> 1], acc_s[nb][i & 1], 0, 0, 0);
     }
-    uint32_t pw[NBW][16];
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) {
+    for (int j = 0; j < kVPF; ++j) vf[j] = v_frag(j);
+#pragma unroll
+    for (int i = 0; i < kKPF; ++i) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+#pragma unroll
+    for (int i = 0; i < kKR; ++i) {
+      if (i + kKPF < kKR) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kNB, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kVPF, 0);
+
+    uint32_t pw[kNB][16];
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
       // causal mask (only on tiles that reach past the block's first position):
       // key key0 + off(r) with off(r) = mb*32 + (r/4)*8 + half*4 + r%4 is
       // visible iff off(r) - half*4 <= pos - key0 - half*4
-      if (key0 + kKT - 1 > w_min_pos + (SHARED ? 0 : 32 * nb)) {
+      if (key0 + kKT - 1 > min_pos[nb]) {
         const int lim = pos[nb] - key0 - half * 4;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
@@ -353,122 +371,75 @@ __global__ __launch_bounds__(256, NBW == 1 ? 2 : 1) void prefill_mfma_kernel(Pre
         lsum[nb] = dot2_bf16(pw[nb][i], kOnes, lsum[nb]);
       }
     }
-    // O^T += V^T P^T; each V^T fragment feeds the NBW column blocks
+    // O^T += V^T P^T; each V^T fragment feeds the kNB column blocks, reads kVPF fragments ahead
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int j = 0; j < kVR; ++j) {
+      if (j + kVPF < kVR) vf[j + kVPF] = v_frag(j + kVPF);
+      const int ks = j / MD, md = j % MD;
 #pragma unroll
-      for (int md = 0; md < MD; ++md) {
-        const bf16x8_t af = __builtin_bit_cast(
-            bf16x8_t, *reinterpret_cast<const uint4*>(&lds_v[buf][(md * 32 + col) * VS + 16 * ks + 8 * half]));
-#pragma unroll
-        for (int nb = 0; nb < NBW; ++nb) {
-          const bf16x8_t bf = __builtin_bit_cast(
-              bf16x8_t, make_uint4(pw[nb][4 * ks], pw[nb][4 * ks + 1], pw[nb][4 * ks + 2], pw[nb][4 * ks + 3]));
-          acc_o[nb][md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc_o[nb][md], 0, 0, 0);
-        }
+      for (int nb = 0; nb < kNB; ++nb) {
+        const bf16x8_t bf = __builtin_bit_cast(
+            bf16x8_t, make_uint4(pw[nb][4 * ks], pw[nb][4 * ks + 1], pw[nb][4 * ks + 2], pw[nb][4 * ks + 3]));
+        acc_o[nb][md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], bf, acc_o[nb][md], 0, 0, 0);
       }
     }
-  };
-
-  const int n_kt_wave = wave_active ? min(n_kt, w_max_pos / kKT + 1) : 0;
-  // block ids of the next tile to load (run one tile ahead of its loads)
-  int32_t bk, bv = 0;
-  auto next_ids = [&](int t) {
-    if constexpr (UT) {
-      bk = tile_block(t * kKT);
-    } else {
-      bk = block_id(t * kKT + k_row);
-      bv = block_id(t * kKT + 4 * v_kg);
+#pragma unroll
+    for (int j = 0; j < kVR; ++j) {
+      if (j + kVPF < kVR) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kNB, 1);
     }
   };
-  next_ids(0);
-#if PKV_PF_DEPTH == 2
-  // Pipeline: while tile kt is computed from LDS, the global loads of tiles
-  // kt+1 and kt+2 are in flight in two register stages (tile t in stage t % 2),
-  // so a load has two tiles' compute time to arrive.  One barrier per tile.
-  // The tiles past this wave's last position are only loaded for the other
-  // waves (the last loop), which keeps the compute loop free of a
-  // data-dependent skip.
-  uint4 a0, a1, a2, a3, a4, a5, a6, a7;  // stage 0
-  uint4 b0, b1, b2, b3, b4, b5, b6, b7;  // stage 1
-#define PKV_S0 a0, a1, a2, a3, a4, a5, a6, a7
-#define PKV_S1 b0, b1, b2, b3, b4, b5, b6, b7
-  issue_loads(PKV_S0, 0, bk, bv);
+
+  constexpr int kCopies = 2 * IPW;  // copy instructions per wave and tile
+  fetch_blocks(0);
+  issue_copies(0, 0);
   if (n_kt > 1) {
-    next_ids(1);
-    issue_loads(PKV_S1, 1, bk, bv);
-    if (n_kt > 2) next_ids(2);
+    fetch_blocks(1);
+    issue_copies(1, 1);
+    if (n_kt > 2) fetch_blocks(2);
   }
-  write_lds(PKV_S0, 0);
-  __syncthreads();
-  if (n_kt > 2) {
-    const int32_t ck = bk, cv = bv;
-    if (n_kt > 3) next_ids(3);
-    issue_loads(PKV_S0, 2, ck, cv);
-  }
-  // tile kt: compute it, move tile kt+1 from its stage `wr` to LDS, refill `wr` with tile kt+3
-  auto step = [&](int kt, PKV_STAGE_PARAMS, bool with_compute) {
-    if (with_compute) compute(kt & 1, kt * kKT);
-    if (kt + 1 < n_kt) write_lds(k0r, k1r, k2r, k3r, v0, v1, v2, v3, (kt & 1) ^ 1);
-    if (kt + 3 < n_kt) {
-      // the next tile's block ids are requested before this tile's rows, so that
-      // waiting for them later never waits for these rows (loads retire in order)
-      const int32_t ck = bk, cv = bv;
-      if (kt + 4 < n_kt) next_ids(kt + 4);
-      issue_loads(k0r, k1r, k2r, k3r, v0, v1, v2, v3, kt + 3, ck, cv);
+  // Q^T, loaded while the first tiles are in flight
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    const uint16_t* qp = (const uint16_t*)a.q + q_row[nb] * D + 8 * half;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (col_valid[nb]) x = *reinterpret_cast<const uint4*>(qp + 16 * kk);
+      qf[nb][kk] = __builtin_bit_cast(bf16x8_t, x);
     }
-    __syncthreads();
-  };
-  int kt = 0;
-  for (; kt + 1 < n_kt_wave; kt += 2) {
-    step(kt, PKV_S1, true);
-    step(kt + 1, PKV_S0, true);
   }
-  if (kt < n_kt_wave) step(kt++, PKV_S1, true);
-  for (; kt < n_kt; ++kt) {
-    if (kt & 1)
-      step(kt, PKV_S0, false);
-    else
-      step(kt, PKV_S1, false);
-  }
-#undef PKV_S0
-#undef PKV_S1
-#else
-  // Pipeline: tile kt+1's global loads are in flight while tile kt is computed
-  // from LDS; block ids run two tiles ahead.  One barrier per tile.
-  uint4 a0, a1, a2, a3, a4, a5, a6, a7;
-#define PKV_S0 a0, a1, a2, a3, a4, a5, a6, a7
-  issue_loads(PKV_S0, 0, bk, bv);
-  if (n_kt > 1) next_ids(1);
-  write_lds(PKV_S0, 0);
-  __syncthreads();
-  auto advance = [&](int kt) {
-    if (kt + 1 < n_kt) {
-      issue_loads(PKV_S0, kt + 1, bk, bv);
-      if (kt + 2 < n_kt) next_ids(kt + 2);
-    }
-  };
-  int kt = 0;
-  for (; kt < n_kt_wave; ++kt) {
-    advance(kt);
-    compute(kt & 1, kt * kKT);
-    if (kt + 1 < n_kt) write_lds(PKV_S0, (kt & 1) ^ 1);
-    __syncthreads();
-  }
-  for (; kt < n_kt; ++kt) {
-    advance(kt);
-    if (kt + 1 < n_kt) write_lds(PKV_S0, (kt & 1) ^ 1);
-    __syncthreads();
-  }
-#undef PKV_S0
-#endif
-#undef PKV_STAGE_PARAMS
 
-  if (!wave_active) return;
+  // The compiler's own wait for these loads happens here, once: inside the
+  // loop it would also wait for every tile copy in flight.
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) asm volatile("" ::"v"(qf[nb][kk]));
+  // Pipeline: tiles kt+1 and kt+2 are in flight (direct to LDS) while tile kt
+  // is computed; one barrier per tile.  At the barrier of tile kt every wave
+  // has finished tile kt-1, so its buffer takes tile kt+2.  Each wave waits
+  // for its own copies of tile kt (those of tile kt+1, issued later, may stay
+  // in flight); the barrier then makes every wave's rows visible.
+  int buf = 0;
+  for (int kt = 0; kt < n_kt; ++kt) {
+    if (kt + 1 < n_kt)
+      wait_vmem<kCopies>();
+    else
+      wait_vmem<0>();
+    __syncthreads();
+    if (kt + 2 < n_kt) issue_copies(kt + 2, buf == 0 ? 2 : buf - 1);
+    if (kt < n_kt_wave) compute(buf, kt * kKT);
+    // the next block ids arrive while this wave waits at the next barrier
+    if (kt + 3 < n_kt) fetch_blocks(kt + 3);
+    buf = buf == 2 ? 0 : buf + 1;
+  }
+
+  if (n_kt_wave == 0) return;
   if constexpr (SHARED) {
     // unnormalised state of each column at slot slot0 + chunk of its member's pair
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) {
+    for (int nb = 0; nb < kNB; ++nb) {
       const float l = halves_sum(lsum[nb]);
       if (!col_valid[nb]) continue;
       const int64_t slot = q_row[nb] * a.ws_stride + a.slot0 + chunk;
@@ -489,9 +460,10 @@ __global__ __launch_bounds__(256, NBW == 1 ? 2 : 1) void prefill_mfma_kernel(Pre
     return;
   }
 #pragma unroll
-  for (int nb = 0; nb < NBW; ++nb) {
+  for (int nb = 0; nb < kNB; ++nb) {
+    const float l = halves_sum(lsum[nb]);
     if (!col_valid[nb]) continue;
-    const float inv = 1.0f / halves_sum(lsum[nb]);
+    const float inv = 1.0f / l;
     uint16_t* op = (uint16_t*)a.out + q_row[nb] * D + half * 4;
 #pragma unroll
     for (int md = 0; md < MD; ++md) {
@@ -507,33 +479,27 @@ __global__ __launch_bounds__(256, NBW == 1 ? 2 : 1) void prefill_mfma_kernel(Pre
   }
 }
 
-}  // namespace
-
-namespace {
-
-int heads_per_wave(int32_t num_q_heads, int32_t num_kv_heads) {
+// Query heads per workgroup: the largest of 8, 4, 2, 1 that divides the group size.
+int heads_per_wg(int32_t num_q_heads, int32_t num_kv_heads) {
   const int G = num_q_heads / num_kv_heads;
-  return (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+  return (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
 }
 
 template <bool SHARED>
 hipError_t launch(const PrefillArgs& a, int32_t head_dim, int64_t blocks, int HW, hipStream_t stream) {
-  constexpr int NBW = PKV_PF_NBW;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  dim3 grid((unsigned)blocks), block(256);
-  const bool ut = !a.block_tables || a.log2_block_size >= 6;  // a 64-key tile never crosses a block
-#define PKV_PREFILL_CASE(DD, HH)                                                                      \
-  if (head_dim == DD && HW == HH) {                                                                   \
-    if (ut)                                                                                           \
-      hipLaunchKernelGGL((prefill_mfma_kernel<DD, HH, NBW, SHARED, true>), grid, block, 0, stream, a);  \
-    else                                                                                              \
-      hipLaunchKernelGGL((prefill_mfma_kernel<DD, HH, NBW, SHARED, false>), grid, block, 0, stream, a); \
-    return hipGetLastError();                                                                         \
+  dim3 grid((unsigned)blocks), block(kThreads);
+#define PKV_PREFILL_CASE(DD, HH)                                                                     \
+  if (head_dim == DD && HW == HH) {                                                                  \
+    hipLaunchKernelGGL((prefill_mfma_kernel<DD, HH, SHARED>), grid, block, 0, stream, a);            \
+    return hipGetLastError();                                                                        \
   }
+  PKV_PREFILL_CASE(128, 8)
   PKV_PREFILL_CASE(128, 4)
   PKV_PREFILL_CASE(128, 2)
   PKV_PREFILL_CASE(128, 1)
+  PKV_PREFILL_CASE(64, 8)
   PKV_PREFILL_CASE(64, 4)
   PKV_PREFILL_CASE(64, 2)
   PKV_PREFILL_CASE(64, 1)
@@ -544,25 +510,27 @@ hipError_t launch(const PrefillArgs& a, int32_t head_dim, int64_t blocks, int HW
 }  // namespace
 
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int32_t head_dim, hipStream_t stream) {
-  const int HW = heads_per_wave(a.num_q_heads, a.num_kv_heads);
-  const int QP = 32 * PKV_PF_NBW * (4 / HW);
-  const int64_t n_qt = (a.max_seqlen_q + QP - 1) / QP;
-  return launch<false>(a, head_dim, n_qt * a.num_seqs * (a.num_q_heads / HW), HW, stream);
+  const int HW = heads_per_wg(a.num_q_heads, a.num_kv_heads);
+  const int QP = 32 * (kCB / HW);
+  PrefillArgs b = a;
+  b.tiles_per_pair = (a.max_seqlen_q + QP - 1) / QP;
+  const int64_t pairs = (int64_t)a.num_seqs * (a.num_q_heads / HW);
+  return launch<false>(b, head_dim, (pairs + kXcds - 1) / kXcds * kXcds * b.tiles_per_pair, HW, stream);
 }
 
 int shared_prefix_members_per_wg(int32_t num_q_heads, int32_t num_kv_heads) {
-  return 32 * PKV_PF_NBW * (4 / heads_per_wave(num_q_heads, num_kv_heads));
+  return 32 * (kCB / heads_per_wg(num_q_heads, num_kv_heads));
 }
 
 int64_t shared_prefix_wgs_per_chunk(int32_t num_q_heads, int32_t num_kv_heads, int32_t num_groups,
                                     int32_t max_group_size) {
   const int per_wg = shared_prefix_members_per_wg(num_q_heads, num_kv_heads);
   const int64_t tiles = ((max_group_size > 1 ? max_group_size : 1) + per_wg - 1) / per_wg;
-  return (int64_t)num_groups * tiles * (num_q_heads / heads_per_wave(num_q_heads, num_kv_heads));
+  return (int64_t)num_groups * tiles * (num_q_heads / heads_per_wg(num_q_heads, num_kv_heads));
 }
 
 hipError_t launch_shared_prefix_mfma(const PrefillArgs& a, int32_t head_dim, hipStream_t stream) {
-  const int HW = heads_per_wave(a.num_q_heads, a.num_kv_heads);
+  const int HW = heads_per_wg(a.num_q_heads, a.num_kv_heads);
   const int64_t blocks = (int64_t)a.num_groups * a.num_chunks * a.member_tiles * (a.num_q_heads / HW);
   return launch<true>(a, head_dim, blocks, HW, stream);
 }
