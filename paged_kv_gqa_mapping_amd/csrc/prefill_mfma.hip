@@ -86,8 +86,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // retire in order).  No memory clobber: every LDS read of a tile buffer is
 // separated from the copies into that buffer by a workgroup barrier (a
 // compiler fence too), and without it the block-table reads stay scalar loads.
+// An LDS-DMA instruction needs one wait state after an SALU write of m0 (the
+// s_nop).  m0 is reserved by the compiler, which keeps no value in it in this
+// file (a build test checks that every m0 write in the kernels is one of these).
 __device__ __forceinline__ void copy_to_lds(const void* g, uint32_t m0) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "m0");
 }
 
 template <int N>
