@@ -123,9 +123,13 @@ DecodePlan cascade_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_he
   }
   p.S = std::max(1, (own + p.split - 1) / p.split);
   if (num_groups > 0 && max_shared_len > 0) {
+    // chunks of the shared prefix: from 256 keys, doubled while the group pass
+    // would have more workgroups than the 256 CUs hold at once (one each: the
+    // pass stages its K/V tiles in 96 KB of LDS); fewer, longer chunks also
+    // leave fewer states per member for the merge
     const int64_t wgs = pkv::shared_prefix_wgs_per_chunk(num_q_heads, num_kv_heads, num_groups, max_group_size);
     p.chunk = 256;
-    while (p.chunk < max_shared_len && wgs * ((max_shared_len + p.chunk - 1) / p.chunk) > 512) p.chunk *= 2;
+    while (p.chunk < max_shared_len && wgs * ((max_shared_len + p.chunk - 1) / p.chunk) > 256) p.chunk *= 2;
     p.C = (max_shared_len + p.chunk - 1) / p.chunk;
   }
   return p;

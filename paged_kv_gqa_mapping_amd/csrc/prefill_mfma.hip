@@ -1,22 +1,23 @@
 // Causal varlen prefill attention on the gfx950 matrix cores (bf16 operands,
 // fp32 accumulation), over paged or packed K/V.
 //
-// Work split: a workgroup (4 waves, one per SIMD) takes one sequence, one group
+// Work split: a workgroup (8 waves, two per SIMD) takes one sequence, one group
 // of HW query heads that share a KV head, and QP = 32 * (8 / HW) consecutive
-// query positions: 8 column blocks of 32 (position, head) columns, block cb =
-// 2 * wave + nb holding head cb % HW and positions 32 * (cb / HW) .. +31 of the
-// tile.  Each wave thus multiplies every K/V operand fragment it reads from LDS
-// into two column blocks.  The workgroup walks the key axis in tiles of 64 keys
-// up to its last query's position; each K and V tile is staged in LDS once for
-// the whole GQA head group.
+// query positions: 8 column blocks of 32 (position, head) columns, wave w
+// holding head w % HW and positions 32 * (w / HW) .. +31 of the tile.  The
+// workgroup walks the key axis in tiles of 64 keys up to its last query's
+// position; each K and V tile is staged in LDS once for the whole GQA head
+// group, i.e. for 256 columns.  The query tiles of one (sequence, head group)
+// run back to back on one XCD, so that they share the K/V tiles through its L2.
 //
 // Tile staging: the global -> LDS copies are direct (global_load_lds_dwordx4:
 // 64 lanes x 16 bytes per instruction), through a ring of 3 tile buffers, so
 // two tiles are in flight while one is computed and no register or VALU work
 // is spent on them.  K and V are stored row-major (one row per key, no
 // padding); the 16-byte slot that holds chunk c of key row k is rotated by
-// the key (K: (c + k) mod D/8; V: (c + 2 (k mod 4)) mod D/8), which keeps the
-// fragment reads below free of bank conflicts.
+// the key (K: (c + k) mod D/8; V: (c + 4 (k mod 4)) mod 16 for D = 128, (c + 4
+// (k / 2 mod 2)) mod 8 for D = 64), which keeps the fragment reads below free
+// of bank conflicts.
 //
 // Per tile and wave, with v_mfma_f32_32x32x16_bf16:
 //   S^T[key][col] = K_tile * Q^T     (2 key blocks x D/16 steps, ds_read_b128)
@@ -52,17 +53,12 @@ namespace {
 constexpr int kKT = 64;   // keys per tile
 constexpr int kCB = 8;    // column blocks per workgroup
 constexpr int kBufs = 3;  // tile buffers in the LDS ring
-#ifndef PKV_PF_XCDS
-#define PKV_PF_XCDS 8
-#endif
-constexpr int kXcds = PKV_PF_XCDS;  // accelerator dies (XCDs), each with its own L2
+constexpr int kXcds = 8;  // accelerator dies (XCDs), each with its own L2
 
-// Column blocks per wave: 1 (8 waves per workgroup, two per SIMD) or 2 (4 waves,
-// one per SIMD, every LDS fragment feeding two MFMAs).
-#ifndef PKV_PF_NB
-#define PKV_PF_NB 1
-#endif
-constexpr int kNB = PKV_PF_NB;
+// Column blocks per wave.  (Two, with four waves per workgroup at one wave per
+// SIMD, would feed every LDS fragment to two MFMAs, but the accumulators then
+// exceed the architectural VGPRs and the code moves them to and from AGPRs.)
+constexpr int kNB = 1;
 constexpr int kWaves = kCB / kNB;
 constexpr int kThreads = 64 * kWaves;
 
@@ -225,6 +221,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
     for (int j = 0; j < NBLK; ++j)
       blk[j] = table[uniform((key_base + min(t * kKT + RW * wave + 8 * j, last_key)) >> lbs)];
   };
+  // rotation (in 16-byte slots) of V row k: the four rows of one transposing
+  // read land in four distinct 64-byte quarters of the 256-byte bank line
+  auto vrot = [](int k) { return D == 128 ? 4 * (k & 3) : 4 * ((k >> 1) & 1); };
   // copy instruction i of tile t into buffer buf: K rows for i < IPW, then V rows
   auto issue_copy = [&](int t, int buf, int i) {
     const int ii = i % IPW;
@@ -233,7 +232,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
     const int tc = min(t * kKT + rt, last_key);
     const int64_t row = table ? (int64_t)blk[(ii * RPI) / 8] * blk_bytes + (int64_t)((key_base + tc) & bs_mask) * row_bytes
                               : (int64_t)(k0 + tc) * row_bytes;
-    const int ch = is_v ? (ls - 2 * (rt & 3)) & (CPR - 1) : (ls - rt) & (CPR - 1);
+    const int ch = is_v ? (ls - vrot(rt)) & (CPR - 1) : (ls - rt) & (CPR - 1);
     const uint32_t dst = lds_addr(&lds[buf][is_v ? 1 : 0][0]) + RW * wave * ROWB + ii * 1024;
     copy_to_lds((is_v ? vbytes : kbytes) + row + head_bytes + 16 * ch, uniform(dst));
   };
@@ -256,7 +255,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
   {
     const int r = lane & 15;
     const int grp = lane >> 4;
-    const int qr = 2 * (grp & 1) + (r & 3) / 2 + 2 * (r >> 2);
+    const int qr = 2 * (grp & 1) + (r & 3) / 2 + vrot(r >> 2);
 #pragma unroll
     for (int md = 0; md < MD; ++md)
       voff[md] = (4 * half + (r >> 2)) * ROWB + 16 * ((4 * md + qr) & (CPR - 1)) + 8 * (r & 1);

@@ -160,13 +160,13 @@ def test_cascade_workspace_bytes():
             L.pkv_decode_workspace_bytes(64, 32, 128, maxL, split)
     # one group of 64 behind 16,384 shared keys with at most 512 keys of its own:
     # 2 split states of 256 keys plus the group-pass states (chunk doubled from 256 while
-    # member tiles x 8 head groups x chunks > 512 workgroups; a group-pass workgroup
-    # takes 64 members for 4 query heads per KV head, so 1 member tile: 256 keys -> 64 chunks)
+    # member tiles x 8 head groups x chunks > 256 workgroups; a group-pass workgroup
+    # takes 64 members for 4 query heads per KV head, so 1 member tile: 512 keys -> 32 chunks)
     assert L.pkv_cascade_workspace_bytes(64, 32, 8, 128, 16896, 512, 256, 1, 64, 16384) == \
-        64 * 32 * (2 + 64) * (128 + 2) * 4
-    # twice the members: 2 member tiles x 8 x 64 chunks > 512, so 512-key chunks -> 32 chunks
+        64 * 32 * (2 + 32) * (128 + 2) * 4
+    # twice the members: 2 member tiles x 8 head groups, so 1024-key chunks -> 16 chunks
     assert L.pkv_cascade_workspace_bytes(128, 32, 8, 128, 16896, 512, 256, 1, 128, 16384) == \
-        128 * 32 * (2 + 32) * (128 + 2) * 4
+        128 * 32 * (2 + 16) * (128 + 2) * 4
 
 
 @needs_lib
