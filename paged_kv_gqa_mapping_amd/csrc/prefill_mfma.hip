@@ -5,14 +5,14 @@
 // of HW query heads that share a KV head, and QP = 32 * (8 / HW) consecutive
 // query positions: 8 column blocks of 32 (position, head) columns, wave w
 // holding head w % HW and positions 32 * (w / HW) .. +31 of the tile.  The
-// workgroup walks the key axis in tiles of 64 keys up to its last query's
+// workgroup walks the key axis in tiles of 128 keys up to its last query's
 // position; each K and V tile is staged in LDS once for the whole GQA head
 // group, i.e. for 256 columns.  The query tiles of one (sequence, head group)
 // run back to back on one XCD, so that they share the K/V tiles through its L2.
 //
 // Tile staging: the global -> LDS copies are direct (global_load_lds_dwordx4:
-// 64 lanes x 16 bytes per instruction), through a ring of 3 tile buffers, so
-// two tiles are in flight while one is computed and no register or VALU work
+// 64 lanes x 16 bytes per instruction) into two tile buffers, so that one
+// tile is in flight while the other is computed, and no register or VALU work
 // is spent on them.  K and V are stored row-major (one row per key, no
 // padding); the 16-byte slot that holds chunk c of key row k is rotated by
 // the key (K: (c + k) mod D/8; V: (c + 4 (k mod 4)) mod 16 for D = 128, (c + 4
@@ -20,11 +20,11 @@
 // of bank conflicts.
 //
 // Per tile and wave, with v_mfma_f32_32x32x16_bf16:
-//   S^T[key][col] = K_tile * Q^T     (2 key blocks x D/16 steps, ds_read_b128)
+//   S^T[key][col] = K_tile * Q^T     (4 key blocks x D/16 steps, ds_read_b128)
 //   online softmax per column: the accumulator gives each lane one column and
 //   16 keys per key block, so the row max and sum are in-lane plus one
 //   half-wave exchange;
-//   O^T[d][col] += V^T * P^T         (D/32 blocks x 4 steps), where P^T is the
+//   O^T[d][col] += V^T * P^T         (D/32 blocks x 8 steps of 16 keys), where P^T is the
 //   S^T accumulator itself, rounded to bf16.  The lane/register layout of an
 //   MFMA result is that of its B operand up to a fixed permutation of the 16
 //   keys of each step; the V^T fragments are read with ds_read_b64_tr_b16
@@ -50,9 +50,13 @@ namespace pkv {
 
 namespace {
 
-constexpr int kKT = 64;   // keys per tile
+// Keys per tile: 128 (4.4 % faster than 64: half the waits, barriers and copy
+// issues per key), in two LDS buffers (128 KiB for D = 128); one tile's copies
+// are in flight while the other is computed, ahead by a tile's compute time.
+constexpr int kKT = 128;
+constexpr int kKB = kKT / 32;  // 32-key blocks per tile
 constexpr int kCB = 8;    // column blocks per workgroup
-constexpr int kBufs = 3;  // tile buffers in the LDS ring
+constexpr int kBufs = 2;  // tile buffers in LDS
 constexpr int kXcds = 8;  // accelerator dies (XCDs), each with its own L2
 
 // Column blocks per wave.  (Two, with four waves per workgroup at one wave per
@@ -282,10 +286,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
   // Scheduling groups (instruction classes of __builtin_amdgcn_sched_group_barrier).
   constexpr int kSchedMfma = 0x008;
   constexpr int kSchedDsRead = 0x100;
-  constexpr int kKR = 2 * KSTEPS;  // K fragment reads per tile
-  constexpr int kKPF = 4;          // K fragment reads in flight
-  constexpr int kVR = 4 * MD;      // V^T fragments per tile (two transposing reads each)
-  constexpr int kVPF = 3;          // V^T fragments in flight
+  constexpr int kKR = kKB * KSTEPS;  // K fragment reads per tile
+  constexpr int kKPF = 4;            // K fragment reads in flight
+  constexpr int kVR = kKT / 16 * MD;  // V^T fragments per tile (two transposing reads each)
+  constexpr int kVPF = 3;            // V^T fragments in flight
 
   auto compute = [&](int buf, int key0) {
     const uint8_t* kt_lds = &lds[buf][0][0];
@@ -293,7 +297,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
     // fragment i of K: step kk = i / 2, key block mb = i % 2
     auto k_frag = [&](int i) {
       return __builtin_bit_cast(bf16x8_t,
-                                *reinterpret_cast<const uint4*>(kt_lds + koff[i >> 1] + (i & 1) * 32 * ROWB));
+                                *reinterpret_cast<const uint4*>(kt_lds + koff[i / kKB] + (i % kKB) * 32 * ROWB));
     };
     // fragment j of V^T: key step ks = j / MD, dim block md = j % MD
     auto v_frag = [&](int j) {
@@ -305,11 +309,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
     // S^T = K Q^T (raw scores); each K fragment feeds the kNB column blocks,
     // and the reads run kKPF fragments ahead of the MFMAs.  The first V^T
     // fragments are requested at the end, so that they arrive during the softmax.
-    f32x16_t acc_s[kNB][2];
+    f32x16_t acc_s[kNB][kKB];
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < kKB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc_s[nb][mb][r] = 0.f;
     bf16x8_t kf[kKR];
@@ -321,7 +325,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
       if (i + kKPF < kKR) kf[i + kKPF] = k_frag(i + kKPF);
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb)
-        acc_s[nb][i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[nb][i >> 1], acc_s[nb][i & 1], 0, 0, 0);
+        acc_s[nb][i % kKB] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[nb][i / kKB], acc_s[nb][i % kKB], 0, 0, 0);
     }
 #pragma unroll
     for (int j = 0; j < kVPF; ++j) vf[j] = v_frag(j);
@@ -334,7 +339,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
     }
     __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kVPF, 0);
 
-    uint32_t pw[kNB][16];
+    uint32_t pw[kNB][kKT / 4];
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
       // causal mask (only on tiles that reach past the block's first position):
@@ -343,14 +348,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
       if (key0 + kKT - 1 > min_pos[nb]) {
         const int lim = pos[nb] - key0 - half * 4;
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < kKB; ++mb)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
             if (mb * 32 + (r >> 2) * 8 + (r & 3) > lim) acc_s[nb][mb][r] = kNegInf;
       }
       float mx = kNegInf;
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < kKB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc_s[nb][mb][r]);
       mx = halves_max(mx) * c;  // c > 0, so the max commutes with the scaling
@@ -364,9 +369,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc_o[nb][md][r] *= alpha;
       }
-      // P^T = 2^(c s - m), rounded to bf16, as the B operand of the four 16-key steps
+      // P^T = 2^(c s - m), rounded to bf16, as the B operand of the 16-key steps
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < kKT / 4; ++i) {
         const float s0 = acc_s[nb][i >> 3][(2 * i) & 15];
         const float s1 = acc_s[nb][i >> 3][(2 * i + 1) & 15];
         pw[nb][i] = pack_bf16x2(exp2_hw(fmaf(s0, c, -m[nb])), exp2_hw(fmaf(s1, c, -m[nb])));
@@ -392,14 +397,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
     }
   };
 
-  constexpr int kCopies = 2 * IPW;  // copy instructions per wave and tile
   fetch_blocks(0);
   issue_copies(0, 0);
-  if (n_kt > 1) {
-    fetch_blocks(1);
-    issue_copies(1, 1);
-    if (n_kt > 2) fetch_blocks(2);
-  }
+  if (n_kt > 1) fetch_blocks(1);
   // Q^T, loaded while the first tiles are in flight
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
@@ -418,23 +418,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
   for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) asm volatile("" ::"v"(qf[nb][kk]));
-  // Pipeline: tiles kt+1 and kt+2 are in flight (direct to LDS) while tile kt
-  // is computed; one barrier per tile.  At the barrier of tile kt every wave
-  // has finished tile kt-1, so its buffer takes tile kt+2.  Each wave waits
-  // for its own copies of tile kt (those of tile kt+1, issued later, may stay
-  // in flight); the barrier then makes every wave's rows visible.
+  // Pipeline: tile kt+1 is in flight (direct to LDS) while tile kt is
+  // computed; one barrier per tile.  At the barrier of tile kt each wave has
+  // waited for its own copies of tile kt (the only ones in flight) and every
+  // wave has finished tile kt-1, whose buffer then takes tile kt+1.
   int buf = 0;
   for (int kt = 0; kt < n_kt; ++kt) {
-    if (kt + 1 < n_kt)
-      wait_vmem<kCopies>();
-    else
-      wait_vmem<0>();
+    wait_vmem<0>();
     __syncthreads();
-    if (kt + 2 < n_kt) issue_copies(kt + 2, buf == 0 ? 2 : buf - 1);
+    if (kt + 1 < n_kt) issue_copies(kt + 1, buf ^ 1);
     if (kt < n_kt_wave) compute(buf, kt * kKT);
     // the next block ids arrive while this wave waits at the next barrier
-    if (kt + 3 < n_kt) fetch_blocks(kt + 3);
-    buf = buf == 2 ? 0 : buf + 1;
+    if (kt + 2 < n_kt) fetch_blocks(kt + 2);
+    buf ^= 1;
   }
 
   if (n_kt_wave == 0) return;
