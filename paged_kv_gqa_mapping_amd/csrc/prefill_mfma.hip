@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
   constexpr int CPR = D / 8;           // 16-byte slots per row
   constexpr int TILEB = kKT * ROWB;    // bytes per K (or V) tile
   constexpr int RPI = 1024 / ROWB;     // rows per copy instruction (4 or 8)
-  constexpr int RW = kKT / kWaves;     // rows of each tile copied by one wave (8 or 16)
+  constexpr int RW = kKT / kWaves;     // rows of each tile copied by one wave
   constexpr int IPW = RW / RPI;        // copy instructions per wave, tile and tensor
   __shared__ __attribute__((aligned(1024))) uint8_t lds[kBufs][2][TILEB];
 
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
   int32_t blk[NBLK];
 #pragma unroll
   for (int j = 0; j < NBLK; ++j) blk[j] = 0;
-  auto fetch_blocks = [&](int t) {
+  auto fetch_blocks = [&](int t) __attribute__((always_inline)) {
     if (!table) return;
 #pragma unroll
     for (int j = 0; j < NBLK; ++j)
@@ -227,9 +227,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
   };
   // rotation (in 16-byte slots) of V row k: the four rows of one transposing
   // read land in four distinct 64-byte quarters of the 256-byte bank line
-  auto vrot = [](int k) { return D == 128 ? 4 * (k & 3) : 4 * ((k >> 1) & 1); };
+  auto vrot = [](int k) __attribute__((always_inline)) { return D == 128 ? 4 * (k & 3) : 4 * ((k >> 1) & 1); };
   // copy instruction i of tile t into buffer buf: K rows for i < IPW, then V rows
-  auto issue_copy = [&](int t, int buf, int i) {
+  auto issue_copy = [&](int t, int buf, int i) __attribute__((always_inline)) {
     const int ii = i % IPW;
     const bool is_v = i >= IPW;
     const int rt = RW * wave + ii * RPI + lr;  // row within the tile
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
     const uint32_t dst = lds_addr(&lds[buf][is_v ? 1 : 0][0]) + RW * wave * ROWB + ii * 1024;
     copy_to_lds((is_v ? vbytes : kbytes) + row + head_bytes + 16 * ch, uniform(dst));
   };
-  auto issue_copies = [&](int t, int buf) {
+  auto issue_copies = [&](int t, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 2 * IPW; ++i) issue_copy(t, buf, i);
   };
@@ -291,16 +291,16 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
   constexpr int kVR = kKT / 16 * MD;  // V^T fragments per tile (two transposing reads each)
   constexpr int kVPF = 3;            // V^T fragments in flight
 
-  auto compute = [&](int buf, int key0) {
+  auto compute = [&](int buf, int key0) __attribute__((always_inline)) {
     const uint8_t* kt_lds = &lds[buf][0][0];
     const uint8_t* vt_lds = &lds[buf][1][0];
     // fragment i of K: step kk = i / 2, key block mb = i % 2
-    auto k_frag = [&](int i) {
+    auto k_frag = [&](int i) __attribute__((always_inline)) {
       return __builtin_bit_cast(bf16x8_t,
                                 *reinterpret_cast<const uint4*>(kt_lds + koff[i / kKB] + (i % kKB) * 32 * ROWB));
     };
     // fragment j of V^T: key step ks = j / MD, dim block md = j % MD
-    auto v_frag = [&](int j) {
+    auto v_frag = [&](int j) __attribute__((always_inline)) {
       const uint8_t* vp = vt_lds + voff[j % MD] + (j / MD) * 16 * ROWB;
       const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(vp));
       const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(vp + 8 * ROWB));
