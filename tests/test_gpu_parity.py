@@ -69,6 +69,8 @@ PREFILL_PAIRS = [(1, 1), (1, 40), (5, 5), (31, 31), (32, 32), (33, 100), (64, 64
                  (97, 300), (200, 700)]
 PREFILL_SHAPES = [
     ("bf16", 32, 8, 128, 256),
+    ("bf16", 64, 8, 128, 16),   # 8 query heads per KV head: 8 heads x 32 positions per workgroup
+    ("bf16", 4, 4, 64, 8),      # no grouping at D = 64: one head x 256 positions per workgroup
     ("bf16", 32, 8, 128, 16),
     ("bf16", 16, 8, 128, 64),
     ("bf16", 8, 8, 128, 32),
