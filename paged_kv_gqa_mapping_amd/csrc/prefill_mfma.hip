@@ -43,6 +43,8 @@
 // o) written to the member's decode workspace, merged later with the states
 // of its own keys.  The shared keys are thus read once per group instead of
 // once per member.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -56,7 +58,16 @@ namespace {
 constexpr int kKT = 128;
 constexpr int kKB = kKT / 32;  // 32-key blocks per tile
 constexpr int kCB = 8;    // column blocks per workgroup
-constexpr int kBufs = 2;  // tile buffers in LDS
+// Skewed schedule: waves 4-7 (which share SIMDs with waves 0-3) multiply a
+// tile's weights by V one tile later, after the next barrier, so that the two
+// waves of a SIMD are in different phases (one on the matrix core, the other
+// in the softmax) instead of in the same one.  V then needs a third buffer.
+#ifndef PKV_PREFILL_SKEW
+#define PKV_PREFILL_SKEW 1
+#endif
+constexpr bool kSkew = PKV_PREFILL_SKEW != 0;
+constexpr int kKBufs = 2;              // K tile buffers in LDS
+constexpr int kVBufs = kSkew ? 3 : 2;  // V tile buffers in LDS
 constexpr int kXcds = 8;  // accelerator dies (XCDs), each with its own L2
 
 // Column blocks per wave.  (Two, with four waves per workgroup at one wave per
@@ -92,6 +103,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 __device__ __forceinline__ void copy_to_lds(const void* g, uint32_t m0) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "m0");
 }
+// The same copy with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane
+// byte offset (the scalar-base form: no per-lane 64-bit address arithmetic).
+__device__ __forceinline__ void copy_to_lds(const void* base, uint32_t off, uint32_t m0) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "s"(m0) : "m0");
+}
 
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
@@ -109,7 +125,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
   constexpr int RPI = 1024 / ROWB;     // rows per copy instruction (4 or 8)
   constexpr int RW = kKT / kWaves;     // rows of each tile copied by one wave
   constexpr int IPW = RW / RPI;        // copy instructions per wave, tile and tensor
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kBufs][2][TILEB];
+  // K tile buffers, then V tile buffers (160 KiB for D = 128 with the skew)
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[(kKBufs + kVBufs) * TILEB];
 
   const int tid = threadIdx.x;
   // wave-uniform (scalar): the tile loop bounds and the block-id lookups derive from it
@@ -228,21 +245,48 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
   // rotation (in 16-byte slots) of V row k: the four rows of one transposing
   // read land in four distinct 64-byte quarters of the 256-byte bank line
   auto vrot = [](int k) __attribute__((always_inline)) { return D == 128 ? 4 * (k & 3) : 4 * ((k >> 1) & 1); };
-  // copy instruction i of tile t into buffer buf: K rows for i < IPW, then V rows
-  auto issue_copy = [&](int t, int buf, int i) __attribute__((always_inline)) {
+  // Per-lane part of copy instruction i's source (the same for every tile):
+  // row lr of the instruction's RPI rows, the KV head, the rotated slot.
+  uint32_t lane_src[2 * IPW];
+#pragma unroll
+  for (int i = 0; i < 2 * IPW; ++i) {
+    const int rt = RW * wave + (i % IPW) * RPI + lr;
+    const int ch = i >= IPW ? (ls - vrot(rt)) & (CPR - 1) : (ls - rt) & (CPR - 1);
+    lane_src[i] = (uint32_t)(lr * row_bytes + head_bytes) + 16 * ch;
+  }
+  // copy instruction i of tile t into its buffers: K rows for i < IPW, then V
+  // rows.  The RPI rows of one instruction start at a multiple of RPI, so they
+  // lie in one block; on a tile that reaches past the last key (whose rows
+  // then clamp to it) each lane computes its own row.
+  auto issue_copy = [&](int t, int vb, int i, bool whole) __attribute__((always_inline)) {
     const int ii = i % IPW;
     const bool is_v = i >= IPW;
-    const int rt = RW * wave + ii * RPI + lr;  // row within the tile
-    const int tc = min(t * kKT + rt, last_key);
-    const int64_t row = table ? (int64_t)blk[(ii * RPI) / 8] * blk_bytes + (int64_t)((key_base + tc) & bs_mask) * row_bytes
-                              : (int64_t)(k0 + tc) * row_bytes;
-    const int ch = is_v ? (ls - vrot(rt)) & (CPR - 1) : (ls - rt) & (CPR - 1);
-    const uint32_t dst = lds_addr(&lds[buf][is_v ? 1 : 0][0]) + RW * wave * ROWB + ii * 1024;
-    copy_to_lds((is_v ? vbytes : kbytes) + row + head_bytes + 16 * ch, uniform(dst));
+    const int bi = is_v ? kKBufs + vb : (t & 1);
+    const uint32_t dst = uniform(lds_addr(&lds[bi * TILEB]) + RW * wave * ROWB + ii * 1024);
+    const uint8_t* src = is_v ? vbytes : kbytes;
+    if (whole) {
+      const int r0 = t * kKT + RW * wave + ii * RPI;  // first row of the instruction
+      const int64_t row0 = table ? (int64_t)blk[(ii * RPI) / 8] * blk_bytes + (int64_t)((key_base + r0) & bs_mask) * row_bytes
+                                 : (int64_t)(k0 + r0) * row_bytes;
+      copy_to_lds(src + row0, lane_src[i], dst);
+    } else {
+      const int rt = RW * wave + ii * RPI + lr;  // row within the tile
+      const int tc = min(t * kKT + rt, last_key);
+      const int64_t row = table ? (int64_t)blk[(ii * RPI) / 8] * blk_bytes + (int64_t)((key_base + tc) & bs_mask) * row_bytes
+                                : (int64_t)(k0 + tc) * row_bytes;
+      const int ch = is_v ? (ls - vrot(rt)) & (CPR - 1) : (ls - rt) & (CPR - 1);
+      copy_to_lds(src + row + head_bytes + 16 * ch, dst);
+    }
   };
-  auto issue_copies = [&](int t, int buf) __attribute__((always_inline)) {
+  auto issue_copies = [&](int t, int vb) __attribute__((always_inline)) {
+    // every row this wave copies of tile t exists
+    if (t * kKT + RW * wave + RW - 1 <= last_key) {
 #pragma unroll
-    for (int i = 0; i < 2 * IPW; ++i) issue_copy(t, buf, i);
+      for (int i = 0; i < 2 * IPW; ++i) issue_copy(t, vb, i, true);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2 * IPW; ++i) issue_copy(t, vb, i, false);
+    }
   };
 
   // Fragment read offsets within a tile buffer.
@@ -291,24 +335,28 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
   constexpr int kVR = kKT / 16 * MD;  // V^T fragments per tile (two transposing reads each)
   constexpr int kVPF = 3;            // V^T fragments in flight
 
-  auto compute = [&](int buf, int key0) __attribute__((always_inline)) {
-    const uint8_t* kt_lds = &lds[buf][0][0];
-    const uint8_t* vt_lds = &lds[buf][1][0];
-    // fragment i of K: step kk = i / 2, key block mb = i % 2
-    auto k_frag = [&](int i) __attribute__((always_inline)) {
-      return __builtin_bit_cast(bf16x8_t,
-                                *reinterpret_cast<const uint4*>(kt_lds + koff[i / kKB] + (i % kKB) * 32 * ROWB));
-    };
-    // fragment j of V^T: key step ks = j / MD, dim block md = j % MD
-    auto v_frag = [&](int j) __attribute__((always_inline)) {
-      const uint8_t* vp = vt_lds + voff[j % MD] + (j / MD) * 16 * ROWB;
-      const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(vp));
-      const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(vp + 8 * ROWB));
-      return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    // S^T = K Q^T (raw scores); each K fragment feeds the kNB column blocks,
-    // and the reads run kKPF fragments ahead of the MFMAs.  The first V^T
-    // fragments are requested at the end, so that they arrive during the softmax.
+  // fragment i of K in buffer kb: step kk = i / kKB, key block mb = i % kKB
+  auto k_frag = [&](int kb, int i) __attribute__((always_inline)) {
+    return __builtin_bit_cast(
+        bf16x8_t, *reinterpret_cast<const uint4*>(&lds[kb * TILEB] + koff[i / kKB] + (i % kKB) * 32 * ROWB));
+  };
+  // fragment j of V^T in V buffer vb: key step ks = j / MD, dim block md = j % MD
+  auto v_frag = [&](int vb, int j) __attribute__((always_inline)) {
+    const uint8_t* vp = &lds[(kKBufs + vb) * TILEB] + voff[j % MD] + (j / MD) * 16 * ROWB;
+    const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(vp));
+    const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4_t*)(vp + 8 * ROWB));
+    return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  bf16x8_t vf[kVR];            // V^T fragments (kVPF + 1 live at a time)
+  uint32_t pw[kNB][kKT / 4];   // the tile's weights P^T as bf16 pairs
+
+  // S^T = K Q^T (raw scores) for K buffer kb, then the online softmax, which
+  // leaves the bf16 weights in pw.  Each K fragment feeds the kNB column
+  // blocks, and the reads run kKPF fragments ahead of the MFMAs.  With PRE,
+  // the first V^T fragments of V buffer vb are requested at the end of the
+  // products, so that they arrive during the softmax.
+  auto qk_softmax = [&](int kb, int key0, int vb, auto PRE) __attribute__((always_inline)) {
+    constexpr bool pre = decltype(PRE)::value;
     f32x16_t acc_s[kNB][kKB];
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb)
@@ -317,19 +365,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc_s[nb][mb][r] = 0.f;
     bf16x8_t kf[kKR];
-    bf16x8_t vf[kVR];
 #pragma unroll
-    for (int i = 0; i < kKPF; ++i) kf[i] = k_frag(i);
+    for (int i = 0; i < kKPF; ++i) kf[i] = k_frag(kb, i);
 #pragma unroll
     for (int i = 0; i < kKR; ++i) {
-      if (i + kKPF < kKR) kf[i + kKPF] = k_frag(i + kKPF);
+      if (i + kKPF < kKR) kf[i + kKPF] = k_frag(kb, i + kKPF);
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb)
         acc_s[nb][i % kKB] =
             __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i], qf[nb][i / kKB], acc_s[nb][i % kKB], 0, 0, 0);
     }
+    if constexpr (pre) {
 #pragma unroll
-    for (int j = 0; j < kVPF; ++j) vf[j] = v_frag(j);
+      for (int j = 0; j < kVPF; ++j) vf[j] = v_frag(vb, j);
+    }
 #pragma unroll
     for (int i = 0; i < kKPF; ++i) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
 #pragma unroll
@@ -337,9 +386,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
       if (i + kKPF < kKR) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, kNB, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kVPF, 0);
+    if constexpr (pre) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kVPF, 0);
 
-    uint32_t pw[kNB][kKT / 4];
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
       // causal mask (only on tiles that reach past the block's first position):
@@ -378,10 +426,19 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
         lsum[nb] = dot2_bf16(pw[nb][i], kOnes, lsum[nb]);
       }
     }
-    // O^T += V^T P^T; each V^T fragment feeds the kNB column blocks, reads kVPF fragments ahead
+  };
+
+  // O^T += V^T P^T for V buffer vb; each V^T fragment feeds the kNB column
+  // blocks, read kVPF fragments ahead (the first ones already requested with PRE).
+  auto pv = [&](int vb, auto PRE) __attribute__((always_inline)) {
+    constexpr bool pre = decltype(PRE)::value;
+    if constexpr (!pre) {
+#pragma unroll
+      for (int j = 0; j < kVPF; ++j) vf[j] = v_frag(vb, j);
+    }
 #pragma unroll
     for (int j = 0; j < kVR; ++j) {
-      if (j + kVPF < kVR) vf[j + kVPF] = v_frag(j + kVPF);
+      if (j + kVPF < kVR) vf[j + kVPF] = v_frag(vb, j + kVPF);
       const int ks = j / MD, md = j % MD;
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) {
@@ -390,6 +447,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
         acc_o[nb][md] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[j], bf, acc_o[nb][md], 0, 0, 0);
       }
     }
+    if constexpr (!pre) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kVPF, 1);
 #pragma unroll
     for (int j = 0; j < kVR; ++j) {
       if (j + kVPF < kVR) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
@@ -421,17 +479,42 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
   // Pipeline: tile kt+1 is in flight (direct to LDS) while tile kt is
   // computed; one barrier per tile.  At the barrier of tile kt each wave has
   // waited for its own copies of tile kt (the only ones in flight) and every
-  // wave has finished tile kt-1, whose buffer then takes tile kt+1.
-  int buf = 0;
-  for (int kt = 0; kt < n_kt; ++kt) {
-    wait_vmem<0>();
-    __syncthreads();
-    if (kt + 1 < n_kt) issue_copies(kt + 1, buf ^ 1);
-    if (kt < n_kt_wave) compute(buf, kt * kKT);
-    // the next block ids arrive while this wave waits at the next barrier
-    if (kt + 2 < n_kt) fetch_blocks(kt + 2);
-    buf ^= 1;
-  }
+  // wave has finished its work on the buffers that the copies of tile kt+1
+  // overwrite: K of tile kt-1, and V of tile kt-1 (two buffers) or of tile
+  // kt-2 (three buffers, where the late waves still read V of tile kt-1 after
+  // the barrier).
+  // V buffers of tiles kt - 1, kt and kt + 1 (rotated each tile, no modulo)
+  auto tile_loop = [&](auto LATE) __attribute__((always_inline)) {
+    constexpr bool is_late = decltype(LATE)::value;
+    int vprev = kVBufs - 1, vcur = 0, vnext = 1 % kVBufs;
+    for (int kt = 0; kt < n_kt; ++kt) {
+      wait_vmem<0>();
+      __syncthreads();
+      if (kt + 1 < n_kt) issue_copies(kt + 1, vnext);
+      if constexpr (is_late) {
+        if (kt >= 1 && kt <= n_kt_wave) pv(vprev, std::false_type{});
+        if (kt < n_kt_wave) qk_softmax(kt & 1, kt * kKT, 0, std::false_type{});
+      } else {
+        if (kt < n_kt_wave) {
+          qk_softmax(kt & 1, kt * kKT, vcur, std::true_type{});
+          pv(vcur, std::true_type{});
+        }
+      }
+      // the next block ids arrive while this wave waits at the next barrier
+      if (kt + 2 < n_kt) fetch_blocks(kt + 2);
+      const int v_free = vprev;
+      vprev = vcur;
+      vcur = vnext;
+      vnext = kVBufs == 3 ? v_free : vprev;
+    }
+    // a late wave's last tile (no copies are in flight any more)
+    if constexpr (is_late)
+      if (n_kt_wave == n_kt && n_kt > 0) pv(vprev, std::false_type{});
+  };
+  if (kSkew && wave >= kWaves / 2)
+    tile_loop(std::true_type{});
+  else
+    tile_loop(std::false_type{});
 
   if (n_kt_wave == 0) return;
   if constexpr (SHARED) {
