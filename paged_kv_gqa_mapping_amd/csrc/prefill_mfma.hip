@@ -66,6 +66,21 @@ constexpr int kCB = 8;    // column blocks per workgroup
 #define PKV_PREFILL_SKEW 1
 #endif
 constexpr bool kSkew = PKV_PREFILL_SKEW != 0;
+// Compile-time tuning knobs (defaults are the measured choice): LDS fragment
+// reads in flight ahead of the MFMAs (K, V^T), and the wave priority taken
+// while a wave issues its matrix products (0: never raised).
+#ifndef PKV_PREFILL_KPF
+#define PKV_PREFILL_KPF 4
+#endif
+#ifndef PKV_PREFILL_VPF
+#define PKV_PREFILL_VPF 3
+#endif
+#ifndef PKV_PREFILL_PRIO
+#define PKV_PREFILL_PRIO 1
+#endif
+#ifndef PKV_PREFILL_PRIO_QK
+#define PKV_PREFILL_PRIO_QK PKV_PREFILL_PRIO
+#endif
 constexpr int kKBufs = 2;              // K tile buffers in LDS
 constexpr int kVBufs = kSkew ? 3 : 2;  // V tile buffers in LDS
 constexpr int kXcds = 8;  // accelerator dies (XCDs), each with its own L2
@@ -331,9 +346,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
   constexpr int kSchedMfma = 0x008;
   constexpr int kSchedDsRead = 0x100;
   constexpr int kKR = kKB * KSTEPS;  // K fragment reads per tile
-  constexpr int kKPF = 4;            // K fragment reads in flight
+  constexpr int kKPF = PKV_PREFILL_KPF;  // K fragment reads in flight
   constexpr int kVR = kKT / 16 * MD;  // V^T fragments per tile (two transposing reads each)
-  constexpr int kVPF = 3;            // V^T fragments in flight
+  constexpr int kVPF = PKV_PREFILL_VPF;  // V^T fragments in flight
 
   // fragment i of K in buffer kb: step kk = i / kKB, key block mb = i % kKB
   auto k_frag = [&](int kb, int i) __attribute__((always_inline)) {
@@ -365,6 +380,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc_s[nb][mb][r] = 0.f;
     bf16x8_t kf[kKR];
+    if constexpr (PKV_PREFILL_PRIO_QK > 0) __builtin_amdgcn_s_setprio(PKV_PREFILL_PRIO_QK);
 #pragma unroll
     for (int i = 0; i < kKPF; ++i) kf[i] = k_frag(kb, i);
 #pragma unroll
@@ -387,6 +403,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, kNB, 0);
     }
     if constexpr (pre) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kVPF, 0);
+    if constexpr (PKV_PREFILL_PRIO_QK > 0) __builtin_amdgcn_s_setprio(0);
 
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
@@ -432,6 +449,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
   // blocks, read kVPF fragments ahead (the first ones already requested with PRE).
   auto pv = [&](int vb, auto PRE) __attribute__((always_inline)) {
     constexpr bool pre = decltype(PRE)::value;
+    if constexpr (PKV_PREFILL_PRIO > 0) __builtin_amdgcn_s_setprio(PKV_PREFILL_PRIO);
     if constexpr (!pre) {
 #pragma unroll
       for (int j = 0; j < kVPF; ++j) vf[j] = v_frag(vb, j);
@@ -453,6 +471,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
       if (j + kVPF < kVR) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 1);
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, kNB, 1);
     }
+    if constexpr (PKV_PREFILL_PRIO > 0) __builtin_amdgcn_s_setprio(0);
   };
 
   fetch_blocks(0);
