@@ -420,14 +420,44 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(RowAttnArgs a) {
   const float* wo = a.ws_o + (int64_t)pair * S * D + lane * EPL;
   // slot of the i-th state: splits 0 .. ns-1, then prefix chunks at num_splits ..
   auto slot = [&](int i) { return i < ns ? i : a.num_splits + (i - ns); };
+  // States are read kBatch at a time, so that their loads are in flight
+  // together (the first batch's with the maxima of the rest: one memory round
+  // trip for up to kBatch states); they are combined one by one in slot order.
+  constexpr int kBatch = 8;
+  const int n = ns + np;
+  float mv[kBatch], lv[kBatch], ov[kBatch][EPL];
+  auto load_batch = [&](int i0) {
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int j = slot(min(i0 + k, n - 1));  // past the end: the last state again, unused
+      mv[k] = ml[2 * j];
+      lv[k] = ml[2 * j + 1];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) ov[k][e] = wo[(int64_t)j * D + e];
+    }
+  };
+  load_batch(0);
   float M = kNegInf;
-  for (int i = 0; i < ns + np; ++i) M = fmaxf(M, ml[2 * slot(i)]);
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k) M = fmaxf(M, mv[k]);  // repeats leave the max alone
+  for (int i0 = kBatch; i0 < n; i0 += kBatch) {
+    float mx[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) mx[k] = ml[2 * slot(min(i0 + k, n - 1))];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) M = fmaxf(M, mx[k]);
+  }
   float den = 0.f, acc[EPL] = {};
-  for (int i = 0; i < ns + np; ++i) {
-    const int j = slot(i);
-    const float w = exp2_hw(ml[2 * j] - M);
-    den = fmaf(w, ml[2 * j + 1], den);
-    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(w, wo[(int64_t)j * D + e], acc[e]);
+  for (int i0 = 0; i0 < n; i0 += kBatch) {
+    if (i0 > 0) load_batch(i0);
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      if (i0 + k >= n) break;
+      const float w = exp2_hw(mv[k] - M);
+      den = fmaf(w, lv[k], den);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(w, ov[k][e], acc[e]);
+    }
   }
   const float inv = 1.0f / den;
   if constexpr (BF16) {
