@@ -7,6 +7,7 @@
 //   PKV_ROW_MAX_ACC  cap on fp32 output accumulators per lane, G * D / (64 / hpw)
 //   PKV_ROW_U        tokens per step (0: 4 for bf16 with G <= 4, else 2)
 //   PKV_ROW_R        step buffers in the load ring (R - 1 steps in flight)
+//   PKV_ROW_NT       1: K/V stream loads marked non-temporal (row_attn.hpp)
 #ifndef PKV_ROW_HPW_MAX
 #define PKV_ROW_HPW_MAX 8
 #endif
