@@ -474,10 +474,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
     if constexpr (PKV_PREFILL_PRIO > 0) __builtin_amdgcn_s_setprio(0);
   };
 
-  fetch_blocks(0);
-  issue_copies(0, 0);
-  if (n_kt > 1) fetch_blocks(1);
-  // Q^T, loaded while the first tiles are in flight
+  // Q^T first: its loads are in flight while the first block ids (scalar
+  // loads) arrive and the first tile's copies are issued
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
     const uint16_t* qp = (const uint16_t*)a.q + q_row[nb] * D + 8 * half;
@@ -488,6 +486,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
       qf[nb][kk] = __builtin_bit_cast(bf16x8_t, x);
     }
   }
+  fetch_blocks(0);
+  issue_copies(0, 0);
+  if (n_kt > 1) fetch_blocks(1);
 
   // The compiler's own wait for these loads happens here, once: inside the
   // loop it would also wait for every tile copy in flight.
