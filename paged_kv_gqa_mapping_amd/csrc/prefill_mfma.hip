@@ -11,9 +11,10 @@
 // run back to back on one XCD, so that they share the K/V tiles through its L2.
 //
 // Tile staging: the global -> LDS copies are direct (global_load_lds_dwordx4:
-// 64 lanes x 16 bytes per instruction) into two tile buffers, so that one
-// tile is in flight while the other is computed, and no register or VALU work
-// is spent on them.  K and V are stored row-major (one row per key, no
+// 64 lanes x 16 bytes per instruction, a wave-uniform base address in SGPRs
+// plus a per-lane offset fixed for the whole launch) into tile buffers (two
+// for K, three for V), so that one tile is in flight while another is
+// computed, with no register staging.  K and V are stored row-major (one row per key, no
 // padding); the 16-byte slot that holds chunk c of key row k is rotated by
 // the key (K: (c + k) mod D/8; V: (c + 4 (k mod 4)) mod 16 for D = 128, (c + 4
 // (k / 2 mod 2)) mod 8 for D = 64), which keeps the fragment reads below free
@@ -53,8 +54,8 @@ namespace pkv {
 namespace {
 
 // Keys per tile: 128 (4.4 % faster than 64: half the waits, barriers and copy
-// issues per key), in two LDS buffers (128 KiB for D = 128); one tile's copies
-// are in flight while the other is computed, ahead by a tile's compute time.
+// issues per key); one tile's copies are in flight while another is
+// computed, ahead by a tile's compute time.
 constexpr int kKT = 128;
 constexpr int kKB = kKT / 32;  // 32-key blocks per tile
 constexpr int kCB = 8;    // column blocks per workgroup
