@@ -6,7 +6,8 @@
 //   PKV_ROW_HPW_MAX  cap on KV heads per wave (8, 4, 2 or 1)
 //   PKV_ROW_MAX_ACC  cap on fp32 output accumulators per lane, G * D / (64 / hpw)
 //   PKV_ROW_U        tokens per step (0: 4 for bf16 with G <= 4, else 2)
-//   PKV_ROW_R        step buffers in the load ring (R - 1 steps in flight)
+//   PKV_ROW_R        step buffers in the load ring (R - 1 steps in flight; 0: 3 for bf16
+//                    decode with G = 4, else 2)
 //   PKV_ROW_NT       1: K/V stream loads marked non-temporal (row_attn.hpp)
 #ifndef PKV_ROW_HPW_MAX
 #define PKV_ROW_HPW_MAX 8
@@ -18,7 +19,7 @@
 #define PKV_ROW_U 0
 #endif
 #ifndef PKV_ROW_R
-#define PKV_ROW_R 2
+#define PKV_ROW_R 0
 #endif
 
 namespace pkv {
@@ -46,16 +47,20 @@ int choose_hpw(int32_t dtype, int32_t head_dim, int32_t num_q_heads, int32_t num
 template <bool BF16, int D, int HPW, int G, bool PREFILL>
 hipError_t launch_one(const RowAttnArgs& a, hipStream_t stream) {
   constexpr int U = PKV_ROW_U ? PKV_ROW_U : ((BF16 && G <= 4) ? 4 : 2);  // tokens per step
+  // load ring depth: with non-temporal K/V loads a 3-deep ring (two steps in
+  // flight, one wave per SIMD) is 1-6 % faster for G = 4 and neutral for G = 2
+  // (G = 8 would need 166 accumulation registers on top of 256 VGPRs)
+  constexpr int R = PKV_ROW_R ? PKV_ROW_R : ((BF16 && G == 4 && !PREFILL) ? 3 : 2);
   const int n_hg = a.num_kv_heads / HPW;
   const int64_t rows = PREFILL ? (int64_t)a.max_rows : (int64_t)a.num_splits;
   const int64_t blocks = (int64_t)n_hg * a.num_seqs * rows;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (!PREFILL && a.k_new)
-    hipLaunchKernelGGL((row_attn_kernel<BF16, D, HPW, G, U, PKV_ROW_R, PREFILL, !PREFILL>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((row_attn_kernel<BF16, D, HPW, G, U, R, PREFILL, !PREFILL>), dim3((unsigned)blocks),
                        dim3(64), 0, stream, a);
   else
-    hipLaunchKernelGGL((row_attn_kernel<BF16, D, HPW, G, U, PKV_ROW_R, PREFILL, false>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((row_attn_kernel<BF16, D, HPW, G, U, R, PREFILL, false>), dim3((unsigned)blocks),
                        dim3(64), 0, stream, a);
   return hipGetLastError();
 }
