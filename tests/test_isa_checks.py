@@ -48,3 +48,24 @@ def test_prefill_kernels_do_not_spill(tmp_path):
     text = _device_asm("prefill_mfma.hip", tmp_path)
     sizes = [int(x) for x in re.findall(r"\.private_segment_fixed_size:\s+(\d+)", text)]
     assert sizes and all(x == 0 for x in sizes), sizes
+
+
+@pytest.mark.skipif(HIPCC is None, reason="hipcc not found")
+def test_bf16_decode_kernels_do_not_spill(tmp_path):
+    # the bf16 decode split pass holds up to three steps of K/V rows in registers
+    # (256 VGPRs plus accumulation registers for four query heads per KV head):
+    # any scratch use there would put memory round trips in the stream
+    text = _device_asm("row_attn.hip", tmp_path)
+    sizes = {}
+    name = None
+    for ln in text.splitlines():
+        m = re.match(r"\s*\.amdhsa_kernel\s+(\S+)", ln)
+        if m:
+            name = m.group(1)
+        m = re.match(r"\s*\.amdhsa_private_segment_fixed_size\s+(\d+)", ln)
+        if m and name:
+            sizes[name] = int(m.group(1))
+    bf16 = {k: v for k, v in sizes.items()
+            if k.startswith("_ZN3pkv15row_attn_kernelILb1E") or k.startswith("_ZN3pkv20decode_reduce_kernelILb1E")}
+    assert len(bf16) >= 10, sorted(sizes)
+    assert all(v == 0 for v in bf16.values()), {k: v for k, v in bf16.items() if v}
