@@ -15,6 +15,7 @@ pytestmark = pytest.mark.gpu
 SHAPES = [
     ("f32", 4, 2, 64, 16), ("f32", 32, 8, 128, 256), ("bf16", 16, 8, 128, 256), ("bf16", 32, 8, 128, 16),
     ("bf16", 8, 1, 128, 32), ("bf16", 16, 2, 64, 8), ("bf16", 64, 8, 128, 64), ("bf16", 4, 4, 64, 16),
+    ("bf16", 16, 4, 64, 32),
 ]
 
 

@@ -45,6 +45,8 @@ DECODE_SHAPES = [
     ("bf16", 16, 2, 64, 8),
     ("bf16", 64, 8, 128, 64),
     ("bf16", 4, 4, 64, 16),
+    ("bf16", 16, 4, 64, 32),    # four query heads per KV head at D = 64 (3-deep load ring, 4 KV heads per wave)
+    ("bf16", 32, 8, 64, 256),   # the same with 8 KV heads per wave
     ("bf16", 8, 2, 128, 1024),  # the largest block size the ABI takes
     ("f32", 8, 2, 64, 8),       # the smallest
 ]
