@@ -101,18 +101,23 @@ def test_prefill_tiny_sweep(shape):
     assert err <= tol(dtype), f"max abs error {err}"
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_prefill_packed_kv(dtype):
-    pairs = [(3, 3), (40, 90), (64, 64), (129, 300), (1, 17)]
+# packed k/v (no block table): group sizes 1-8, both head dims; the last pair walks 12 key tiles
+PACKED_SHAPES = [("bf16", 16, 4, 128), ("f32", 16, 4, 128), ("bf16", 64, 8, 128), ("bf16", 8, 8, 64),
+                 ("bf16", 16, 8, 64), ("f32", 8, 2, 64)]
+
+
+@pytest.mark.parametrize("shape", PACKED_SHAPES, ids=lambda s: "-".join(map(str, s)))
+def test_prefill_packed_kv(shape):
+    dtype, hq, hkv, d = shape
+    pairs = [(3, 3), (40, 90), (64, 64), (129, 300), (1, 17), (70, 1500)]
     lq = [a for a, _ in pairs]
     lk = [b for _, b in pairs]
     cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
     cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
-    hq, hkv, d = 16, 4, 128
     q = W.fill_normal((int(cu_q[-1]), hq, d), dtype, 9, 1)
     k = W.fill_normal((int(cu_k[-1]), hkv, d), dtype, 9, 2)
     v = W.fill_normal((int(cu_k[-1]), hkv, d), dtype, 9, 3)
-    log(f"prefill packed {dtype}")
+    log(f"prefill packed {shape}")
     out = torch.empty((int(cu_q[-1]), hq, d), dtype=torch.bfloat16 if dtype == "bf16" else torch.float32,
                       device="cuda")
     pkv.paged_prefill_attn(to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype), to_dev(cu_q), to_dev(cu_k), None,
