@@ -48,7 +48,8 @@ def _shared_case(hq, hkv, d, bs, n, prefix_blocks, seed, big_group=False):
                    shared_prefix_blocks=prefix_blocks, perm_rng=rng)
 
 
-SHAPES = [(32, 8, 128, 16), (16, 8, 128, 256), (8, 1, 128, 32), (16, 2, 64, 8), (4, 4, 64, 16), (64, 8, 128, 64)]
+SHAPES = [(32, 8, 128, 16), (16, 8, 128, 256), (8, 1, 128, 32), (16, 2, 64, 8), (4, 4, 64, 16), (64, 8, 128, 64),
+          (16, 4, 64, 32)]
 
 
 @pytest.mark.parametrize("split", [0, 64])
