@@ -4,12 +4,12 @@
  * Three operations of a block-paged inference engine's attention layer, as
  * the nano-vLLM pages describe them: the KV-cache write through a slot
  * mapping, decode attention over the paged cache, and causal varlen prefill
- * attention ("Uses the flash-attn library for both prefill ... and decode
- * ... A custom Triton kernel ... writes KV cache entries into the paged
- * cache blocks", "Nano-vLLM Architecture and Performance", section
- * "FlashAttention Integration"; "Attention stores the newly computed K/V into
- * the KV Cache, then uses FlashAttention", "Project overview and the
- * four-layer architecture", section "Lifecycle of one request", step 4).
+ * attention ("Nano-vLLM Architecture and Performance", section
+ * "FlashAttention Integration": prefill and decode attention run through one
+ * attention library and a separate store kernel puts each new token's K/V
+ * into its cache block; "Project overview and the four-layer architecture",
+ * section "Lifecycle of one request", step 4: the new K/V are stored first and
+ * attention runs afterwards).
  *
  * Conventions for every call
  * --------------------------
@@ -29,7 +29,7 @@
  *   block_tables[b * max_blocks_per_seq + p / block_size], row p % block_size;
  *   its slot is block * block_size + row.
  * - GQA: query head h reads KV head h / (num_q_heads / num_kv_heads) (X-Ray
- *   panel of the nano-vllm README: 32 query heads share 8 KV heads).
+ *   panel of the nano-vllm README: 32 query heads over 8 KV heads, four per group).
  * - Supported shapes: head_dim 64 or 128; block_size a power of two in
  *   [8, 1024]; num_q_heads / num_kv_heads in {1, 2, 4, 8}; 1 <= num_kv_heads <= 64.
  *   Other shapes return PKV_ERR_UNSUPPORTED.
@@ -74,10 +74,9 @@ const char* pkv_last_error(void);
 
 /*
  * kv_store -- write the K and V rows of num_tokens new tokens into the paged
- * caches ("store_kvcache_kernel ... writes KV cache entries into the paged
- * cache blocks", "Nano-vLLM Architecture and Performance", section
- * "FlashAttention Integration"; ModelRunner builds the slot_mapping, section
- * "How It Works End-to-End").
+ * caches (the store kernel of "Nano-vLLM Architecture and Performance",
+ * section "FlashAttention Integration"; ModelRunner builds the slot_mapping,
+ * section "How It Works End-to-End").
  *
  *   k, v          [num_tokens, num_kv_heads, head_dim], contiguous, read only.
  *   k_cache,
@@ -130,9 +129,9 @@ int pkv_rope_kv_store(void* q, const void* k, const void* v, const int32_t* posi
  * Decode attention, split-K.  Sequence b's single query q[b] attends all
  * context_lens[b] tokens of its context (the token just stored included),
  * read through row b of block_tables: out = softmax(scale * q K^T) V per
- * query head ("decode computes one token per sequence per step and is
- * memory-bound", "Project overview and the four-layer architecture", section
- * "Lifecycle of one request").
+ * query head (decode produces a single token per sequence each step and is
+ * bound by memory traffic: "Project overview and the four-layer
+ * architecture", section "Lifecycle of one request").
  *
  * The context is cut into splits of split_tokens tokens; each split's
  * unnormalised softmax state (running max, sum, weighted V) goes to the
@@ -246,7 +245,9 @@ int pkv_paged_decode_store_attn(const void* q, const void* k, const void* v, voi
  *                  sizes and split_tokens as the call).
  * With num_groups == 0 or max_shared_len == 0 this is pkv_paged_decode_attn
  * (shared_lens, group_offsets and group_seqs are not read).  The group pass
- * needs dtype PKV_BF16 (PKV_ERR_UNSUPPORTED otherwise).  The device-side
+ * needs dtype PKV_BF16 (PKV_ERR_UNSUPPORTED otherwise) and a scale > 0
+ * (PKV_ERR_INVALID_ARG otherwise: it takes the maximum of unscaled scores and
+ * masks keys past a chunk's end with -inf).  The device-side
  * preconditions above are not checked.
  */
 int pkv_cascade_decode_attn(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
@@ -267,10 +268,10 @@ int64_t pkv_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32
  * Causal varlen prefill attention (chunked prefill and cached prefixes).
  * Sequence b has Lq = cu_seqlens_q[b+1] - cu_seqlens_q[b] new queries and
  * Lk = cu_seqlens_k[b+1] - cu_seqlens_k[b] keys in all, Lq <= Lk.  Query i
- * sits at position Lk - Lq + i and attends keys 0 .. Lk - Lq + i (the causal
- * rule "tokens can only see past tokens", nano-vllm README, tutorial chapter
- * "Self-Attention"; aligned to the newest token so that a chunk after a
- * cached prefix gives what full recomputation would, README section on the
+ * sits at position Lk - Lq + i and attends keys 0 .. Lk - Lq + i (causal: a
+ * query attends keys at positions up to its own, nano-vllm README, tutorial
+ * chapter "Self-Attention"; aligned to the newest token so that a chunk after
+ * a cached prefix gives what full recomputation would, README section on the
  * KV cache: only the new tokens are computed).
  *
  *   q             [total_q, num_q_heads, head_dim], rows cu_seqlens_q[b] + i
@@ -314,10 +315,10 @@ int pkv_paged_gather(const void* k_cache, const void* v_cache, const int32_t* bl
 /*
  * Block manager (host memory only; no device work).  Hands out the physical
  * blocks of a paged KV cache and builds the block tables and slot mappings
- * the calls above consume ("KV cache is divided into fixed-size blocks ...
- * managed by a BlockManager: blocks are allocated on demand as sequences
- * grow; prefix caching ... cached KV blocks are reused (reference-counted)",
- * "Nano-vLLM Architecture and Performance", section "Paged KV Cache").
+ * the calls above consume ("Nano-vLLM Architecture and Performance", section
+ * "Paged KV Cache": the cache is cut into fixed-size blocks that a block
+ * manager hands out as sequences grow, and blocks holding a common prefix are
+ * reused under reference counts).
  *
  * - Blocks have reference counts.  A sequence's full prompt blocks are
  *   looked up in a prefix cache keyed by a hash chained over the token ids of

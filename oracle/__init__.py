@@ -9,18 +9,17 @@ What it computes, step by step, is the plain definition of each operation,
 written for a reader to check by eye; nothing is blocked, fused or reordered:
 
 * ``kv_store`` — write each appended token's K and V row to the slot the slot
-  mapping names ("A custom Triton kernel (store_kvcache_kernel) efficiently
-  writes KV cache entries into the paged cache blocks", "Nano-vLLM
-  Architecture and Performance", section "FlashAttention Integration"; the
-  store happens before attention, "Project overview and the four-layer
-  architecture", section "Lifecycle of one request", step 4).
+  mapping names (the store kernel that fills the paged cache blocks,
+  "Nano-vLLM Architecture and Performance", section "FlashAttention
+  Integration"; the store happens before attention, "Project overview and the
+  four-layer architecture", section "Lifecycle of one request", step 4).
 * ``gather`` — read a sequence's logical tokens back through its block table
   (the "PagedAttention: Allocate blocks on-demand" diagram of the nano-vllm
   README; blocks of a sequence need not be contiguous).
 * ``decode`` / ``prefill`` — scaled dot-product attention ``softmax(q K^T *
   scale) V`` (the X-Ray mode panel "Compute Attention Scores" of the nano-vllm
   README divides the scores by the square root of the head dimension), with
-  grouped-query head sharing (same panel: 32 query heads share 8 KV heads) and
+  grouped-query head sharing (same panel: 32 query heads over 8 KV heads) and
   the causal rule that a token sees only earlier tokens and itself (the
   Self-Attention quiz of the README's tutorial mode).
 

@@ -392,6 +392,10 @@ int pkv_cascade_decode_attn(const void* q, const void* k_cache, const void* v_ca
     if (max_shared_len % block_size)
       return fail(PKV_ERR_INVALID_ARG, "max_shared_len %d is not a whole number of blocks of %d", max_shared_len,
                   block_size);
+    // the group pass takes the max of raw scores before scaling and masks keys
+    // past a chunk's end with -inf, both of which need a positive scale
+    if (!(scale > 0.f) || !std::isfinite(scale))
+      return fail(PKV_ERR_INVALID_ARG, "shared-prefix decode needs a finite scale > 0 (got %g)", (double)scale);
   }
   if (split_tokens < 0 || split_tokens % 64)
     return fail(PKV_ERR_INVALID_ARG, "split_tokens %d is not 0 or a positive multiple of 64", split_tokens);

@@ -108,20 +108,5 @@ def oracle_decode(w: W.Workload, kc, vc, rows=None):
                          w.block_size)
 
 
-def oracle_prefill_rows(w: W.Workload, kc, vc, seq: int, rows) -> np.ndarray:
-    """fp64 prefill output of selected query rows (indices within sequence ``seq``)."""
-    q0 = int(w.cu_seqlens_q[seq])
-    lq = int(w.cu_seqlens_q[seq + 1]) - q0
-    lk = int(w.cu_seqlens_k[seq + 1] - w.cu_seqlens_k[seq])
-    out = []
-    for i in rows:
-        p = lk - lq + i
-        # one query row is a decode over its first p + 1 keys
-        o = oracle.decode(w.pre_q[q0 + i:q0 + i + 1], kc, vc, w.pre_block_tables[seq:seq + 1],
-                          np.array([p + 1], np.int32), w.scale, w.dtype, w.block_size)
-        out.append(o[0])
-    return np.stack(out)
-
-
 def max_abs(gpu: np.ndarray, ref: np.ndarray, dtype: str) -> float:
     return float(np.max(np.abs(W.to_float32(gpu, dtype).astype(np.float64) - ref))) if ref.size else 0.0

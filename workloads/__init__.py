@@ -16,7 +16,7 @@ built):
 * A token at absolute position ``p`` of a sequence lives in physical block
   ``table[p // block_size]`` at row ``p % block_size``; its *slot* is
   ``block * block_size + row`` ("PagedAttention" diagram of the nano-vllm
-  README, and "ModelRunner prepares ... slot mappings, block tables" on
+  README; the model runner builds slot mappings and block tables per step,
   "Nano-vLLM Architecture and Performance", section "How It Works End-to-End").
 * Physical ids are a seeded permutation of the pool, dealt to sequences in
   order; table entries past a sequence's last block point at a poison block.
@@ -118,9 +118,9 @@ class BlockPool:
 
     Blocks are handed out in the order of ``order`` (a seeded permutation), a
     shared block has its count raised once per extra owner, and a block goes
-    back to the free list when its count reaches zero ("Prefix caching ...
-    cached KV blocks are reused (reference-counted)", "Nano-vLLM Architecture
-    and Performance", section "Paged KV Cache").
+    back to the free list when its count reaches zero (blocks of a cached
+    prefix are reused under reference counts: "Nano-vLLM Architecture and
+    Performance", section "Paged KV Cache").
     """
 
     def __init__(self, order):
