@@ -171,6 +171,41 @@ int pkv_paged_decode_attn(const void* q, const void* k_cache, const void* v_cach
                           int32_t head_dim, int64_t num_blocks, int32_t block_size, int32_t dtype,
                           int32_t split_tokens, void* workspace, int64_t workspace_bytes, void* stream);
 
+/*
+ * Allocation-free decode, for callers that cannot allocate device memory or
+ * pass a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): pkv_paged_decode_attn with the split-K
+ * states kept in a scratch array inside the library instead of a caller
+ * workspace.  Same arguments, minus workspace and workspace_bytes; same
+ * kernels, so the results are bit-identical to pkv_paged_decode_attn with the
+ * same split_tokens.
+ *
+ * - The scratch is pkv_noalloc_scratch_bytes() = 64 MiB per GPU, a static
+ *   device array: each GPU the library runs on holds its own copy until the
+ *   process ends.  Nothing is allocated or freed by the call.
+ * - A call whose split states need more than that returns PKV_ERR_WORKSPACE
+ *   before anything is enqueued (raise split_tokens, or use
+ *   pkv_paged_decode_attn).  The states take num_seqs * num_q_heads * S *
+ *   (head_dim + 2) * 4 bytes, S = ceil(max_context_len / split).
+ * - Every call on one GPU shares that GPU's scratch: calls that overlap in
+ *   time on one GPU (on different streams, or from several threads without
+ *   ordering) race and give undefined results.  Calls ordered on one stream
+ *   are safe; each call's states are written before they are read, so
+ *   nothing needs clearing between calls.
+ * - The device that is current on the calling thread must be the stream's
+ *   (PKV_ERR_INVALID_ARG otherwise); its scratch address is looked up on the
+ *   first call on that device.
+ */
+int pkv_paged_decode_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, int32_t max_context_len, float scale, void* out,
+                                  int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int64_t num_blocks, int32_t block_size, int32_t dtype, int32_t split_tokens,
+                                  void* stream);
+
+/* Bytes of the per-GPU scratch of pkv_paged_decode_attn_noalloc. */
+int64_t pkv_noalloc_scratch_bytes(void);
+
 /* The two passes of pkv_paged_decode_attn, enqueued separately (same
  * arguments; call split then reduce on one stream).  Together they do
  * exactly what pkv_paged_decode_attn does. */

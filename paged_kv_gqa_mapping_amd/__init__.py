@@ -33,6 +33,8 @@ import os
 __all__ = [
     "kv_store",
     "paged_decode_attn",
+    "paged_decode_attn_noalloc",
+    "noalloc_scratch_bytes",
     "paged_decode_split",
     "paged_decode_reduce",
     "paged_prefill_attn",
@@ -116,6 +118,10 @@ def lib() -> ctypes.CDLL:
     for name in ("pkv_paged_decode_attn", "pkv_paged_decode_split", "pkv_paged_decode_reduce"):
         getattr(L, name).argtypes = dec
         getattr(L, name).restype = ctypes.c_int
+    L.pkv_paged_decode_attn_noalloc.argtypes = dec[:-3] + [V]
+    L.pkv_paged_decode_attn_noalloc.restype = ctypes.c_int
+    L.pkv_noalloc_scratch_bytes.argtypes = []
+    L.pkv_noalloc_scratch_bytes.restype = I64
     L.pkv_paged_prefill_attn.argtypes = [P, P, P, P, P, P, I32, P, F, I32, I64, I32, I32, I32, I32, I32, I64, I32,
                                          I32, V]
     L.pkv_paged_prefill_attn.restype = ctypes.c_int
@@ -281,6 +287,35 @@ def paged_decode_attn(q, k_cache, v_cache, block_tables, context_lens, scale, ou
     """Decode attention: q [B, Hq, D] over each sequence's context_lens[b] cached tokens -> out [B, Hq, D]."""
     return _decode("pkv_paged_decode_attn", q, k_cache, v_cache, block_tables, context_lens, scale, out,
                    max_context_len, split_tokens, workspace)
+
+
+def paged_decode_attn_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale, out, max_context_len=None,
+                              split_tokens=0):
+    """paged_decode_attn with the split states in the library's per-GPU scratch
+    (no workspace, nothing allocated); calls overlapping on one GPU race."""
+    _dev(q, "q", ndim=3)
+    _dev(k_cache, "k_cache", q.dtype, 4)
+    _dev(v_cache, "v_cache", q.dtype, 4)
+    _dev(block_tables, "block_tables", _torch().int32, 2)
+    _dev(context_lens, "context_lens", _torch().int32, 1)
+    _dev(out, "out", q.dtype, 3)
+    B, Hq, D = q.shape
+    NB, bs, Hkv, D2 = k_cache.shape
+    if v_cache.shape != k_cache.shape or D2 != D or out.shape != q.shape:
+        raise ValueError("shape mismatch among q, k_cache, v_cache, out")
+    if block_tables.shape[0] != B or context_lens.shape[0] != B:
+        raise ValueError("block_tables and context_lens need one row per sequence")
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if B else 0
+    _check(lib().pkv_paged_decode_attn_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        int(max_context_len), float(scale), _ptr(out), B, Hq, Hkv, D, NB, bs, _dtype_code(q), int(split_tokens),
+        _stream()))
+    return out
+
+
+def noalloc_scratch_bytes() -> int:
+    return int(lib().pkv_noalloc_scratch_bytes())
 
 
 def paged_decode_split(q, k_cache, v_cache, block_tables, context_lens, scale, out, max_context_len=None,

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/pkv.h"
@@ -342,6 +343,83 @@ int pkv_paged_decode_reduce(PKV_DECODE_ARGS) {
 int pkv_paged_decode_attn(PKV_DECODE_ARGS) {
   DecodeCall call;
   int st = prepare_decode(call, PKV_DECODE_FWD);
+  if (st || call.empty) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = hip_status(pkv::launch_row_attn(call.args, call.dtype, call.head_dim, false, s), "decode split launch");
+  if (st || call.args.num_splits <= 1) return st;
+  return hip_status(pkv::launch_decode_reduce(call.args, call.dtype, call.head_dim, s), "decode reduce launch");
+}
+
+// ---------------------------------------------------------------- allocation-free decode
+//
+// pkv_paged_decode_attn_noalloc keeps the split-K states in `scratch`, a
+// file-scope device array: each GPU the library runs on holds one copy of it
+// until the process ends.  Host code never passes the array's name to a
+// kernel (on the host that name is only a stand-in): the device address of
+// each GPU's copy comes from hipGetSymbolAddress, taken once per device with
+// that device current, and every use goes through it.
+}  // extern "C"
+
+namespace {
+constexpr int64_t kScratchBytes = 64ll << 20;  // the limit stated in pkv.h
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];  // device address of each GPU's copy (nullptr until its first call)
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+// This device's copy of the scratch array; the stream must belong to the current device.
+int scratch_of_current_device(void* stream, void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (stream) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+    if (e != hipSuccess) return hip_status(e, "hipStreamGetDevice");
+    if (sdev != dev)
+      return fail(PKV_ERR_INVALID_ARG, "the stream belongs to device %d but device %d is current", (int)sdev, dev);
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(PKV_ERR_UNSUPPORTED, "device %d beyond the first %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
+  return PKV_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int64_t pkv_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int pkv_paged_decode_attn_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                                  int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
+                                  float scale, void* out, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int64_t num_blocks, int32_t block_size, int32_t dtype,
+                                  int32_t split_tokens, void* stream) {
+  void* ws = nullptr;
+  int st = scratch_of_current_device(stream, &ws);
+  if (st) return st;
+  DecodeCall call;
+  st = prepare_decode(call, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, max_context_len, scale,
+                      out, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, dtype, split_tokens,
+                      ws, kScratchBytes);
+  if (st == PKV_ERR_WORKSPACE) {
+    // (the sizes were valid: the workspace is checked after them)
+    const int32_t split = split_tokens ? split_tokens : auto_split(num_seqs, num_kv_heads, max_context_len);
+    const int64_t S = (max_context_len + (int64_t)split - 1) / split;
+    return fail(PKV_ERR_WORKSPACE,
+                "the split states of this call need %lld bytes, above the %lld-byte scratch of the allocation-free "
+                "entry point: raise split_tokens or use pkv_paged_decode_attn with a workspace",
+                (long long)state_bytes(num_seqs, num_q_heads, head_dim, S, 0), (long long)kScratchBytes);
+  }
   if (st || call.empty) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = hip_status(pkv::launch_row_attn(call.args, call.dtype, call.head_dim, false, s), "decode split launch");
