@@ -253,8 +253,11 @@ def report(iters: int = 7) -> None:
             pq = dev(w.pre_q, bf)
             pbt, cuq, cuk = dev(w.pre_block_tables, False), dev(w.cu_seqlens_q, False), dev(w.cu_seqlens_k, False)
             pout = torch.empty_like(pq)
+            pws = torch.empty(max(pkv.prefill_workspace_bytes(len(w.cu_seqlens_q) - 1, w.max_seqlen_q, w.num_q_heads,
+                                                              hkv, d, 1 if bf else 0), 256),
+                              dtype=torch.uint8, device="cuda")
             t_pre = timed(lambda: pkv.paged_prefill_attn(pq, kc, vc, cuq, cuk, pbt, pout, max_seqlen_q=w.max_seqlen_q,
-                                                         max_seqlen_k=w.max_seqlen_k, scale=w.scale))
+                                                         max_seqlen_k=w.max_seqlen_k, scale=w.scale, workspace=pws))
             fl = w.prefill_flops()
             rec["prefill_us"] = round(t_pre * 1e3, 2)
             rec["prefill_TFLOP/s"] = round(fl / (t_pre * 1e-3) / 1e12, 1)
@@ -300,6 +303,8 @@ def main():
     ap.add_argument("--overlap-prefill", action="store_true",
                     help="run prefill on a second stream concurrently with decode (after kv_store); the decode "
                          "kernel then shares the GPU, so its event time is not the kernel's own")
+    ap.add_argument("--prefill-persistent", action="store_true",
+                    help="prefill with the planned persistent kernel (workspace) instead of the one-launch kernel")
     ap.add_argument("--graph", action="store_true",
                     help="capture the step in a HIP graph and time graph replays (per-kernel events are not recorded)")
     ap.add_argument("--report", action="store_true",
@@ -369,6 +374,16 @@ def main():
     if has_pre:
         pq, pbt, cuq, cuk = dev(w.pre_q, bf), dev(w.pre_block_tables), dev(w.cu_seqlens_q), dev(w.cu_seqlens_k)
         pout = torch.empty_like(pq)
+        pws = None
+        if args.prefill_persistent:
+            need = pkv.prefill_workspace_bytes(int(len(w.cu_seqlens_q) - 1), w.max_seqlen_q, w.num_q_heads,
+                                               w.num_kv_heads, w.head_dim, 1 if bf else 0)
+            pws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+
+        def prefill():
+            pkv.paged_prefill_attn(pq, kc, vc, cuq, cuk, pbt, pout, max_seqlen_q=w.max_seqlen_q,
+                                   max_seqlen_k=w.max_seqlen_k, scale=w.scale, workspace=pws,
+                                   persistent=args.prefill_persistent)
     torch.cuda.synchronize()
     log("inputs resident on the GPU")
 
@@ -395,12 +410,10 @@ def main():
             s_pre.wait_stream(torch.cuda.current_stream())
             with torch.cuda.stream(s_pre):
                 rec(5)
-                pkv.paged_prefill_attn(pq, kc, vc, cuq, cuk, pbt, pout, max_seqlen_q=w.max_seqlen_q,
-                                       max_seqlen_k=w.max_seqlen_k, scale=w.scale)
+                prefill()
                 rec(6)
         elif has_pre:
-            pkv.paged_prefill_attn(pq, kc, vc, cuq, cuk, pbt, pout, max_seqlen_q=w.max_seqlen_q,
-                                   max_seqlen_k=w.max_seqlen_k, scale=w.scale)
+            prefill()
         rec(2)
         if has_dec and args.cascade:
             cascade_decode(dout)

@@ -324,15 +324,33 @@ int64_t pkv_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32
  *   max_seqlen_q,
  *   max_seqlen_k  host bounds on Lq and Lk over the sequences.
  *
+ *   workspace     NULL, or device scratch of at least
+ *                 pkv_prefill_workspace_bytes(num_seqs, max_seqlen_q, num_q_heads,
+ *                 num_kv_heads, head_dim, dtype) bytes, 256-byte aligned (its
+ *                 contents on entry do not matter; PKV_ERR_WORKSPACE if too small).
+ *
  * bf16 runs on the matrix cores (bf16 operands, fp32 accumulation, the
  * softmax weights rounded to bf16 before they multiply V); fp32 runs on the
- * vector units in fp32.
+ * vector units in fp32 and ignores the workspace.
+ *
+ * With a workspace (bf16), a planning kernel reads cu_seqlens on the device
+ * and writes per-die work lists into it, and a persistent kernel (one
+ * workgroup per compute unit) works through them: sequences with the most
+ * keys first, long query tiles cut along their keys into pieces whose
+ * partial softmax states are merged (in piece order, so results are
+ * deterministic).  Without one, each query tile is a workgroup of a single
+ * launch.  Both compute the same function within rounding; the split and
+ * merge change the rounding order, not the result's definition.
  */
+int64_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t max_seqlen_q, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t dtype);
+
 int pkv_paged_prefill_attn(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
                            const int32_t* cu_seqlens_k, const int32_t* block_tables, int32_t max_blocks_per_seq,
                            void* out, float scale, int32_t num_seqs, int64_t total_q, int32_t max_seqlen_q,
                            int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                           int64_t num_blocks, int32_t block_size, int32_t dtype, void* stream);
+                           int64_t num_blocks, int32_t block_size, int32_t dtype, void* workspace,
+                           int64_t workspace_bytes, void* stream);
 
 /*
  * Block gather (a check of the paged addressing every kernel uses): copy the

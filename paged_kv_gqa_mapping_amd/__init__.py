@@ -38,6 +38,7 @@ __all__ = [
     "paged_decode_split",
     "paged_decode_reduce",
     "paged_prefill_attn",
+    "prefill_workspace_bytes",
     "paged_gather",
     "rope_kv_store",
     "cascade_decode_attn",
@@ -123,8 +124,10 @@ def lib() -> ctypes.CDLL:
     L.pkv_noalloc_scratch_bytes.argtypes = []
     L.pkv_noalloc_scratch_bytes.restype = I64
     L.pkv_paged_prefill_attn.argtypes = [P, P, P, P, P, P, I32, P, F, I32, I64, I32, I32, I32, I32, I32, I64, I32,
-                                         I32, V]
+                                         I32, P, I64, V]
     L.pkv_paged_prefill_attn.restype = ctypes.c_int
+    L.pkv_prefill_workspace_bytes.argtypes = [I32, I32, I32, I32, I32, I32]
+    L.pkv_prefill_workspace_bytes.restype = I64
     L.pkv_paged_gather.argtypes = [P, P, P, I32, P, I32, I32, P, P, I32, I32, I64, I32, I32, V]
     L.pkv_paged_gather.restype = ctypes.c_int
     L.pkv_bm_create.argtypes = [I64, I32, I32]
@@ -399,9 +402,18 @@ def cascade_decode_attn(q, k_cache, v_cache, block_tables, context_lens, shared_
         workspace.numel() * workspace.element_size(), _stream()))
 
 
+def prefill_workspace_bytes(num_seqs, max_seqlen_q, num_q_heads, num_kv_heads, head_dim, dtype_code) -> int:
+    return int(lib().pkv_prefill_workspace_bytes(num_seqs, max_seqlen_q, num_q_heads, num_kv_heads, head_dim,
+                                                 dtype_code))
+
+
 def paged_prefill_attn(q, k, v, cu_seqlens_q, cu_seqlens_k, block_tables, out, max_seqlen_q=None,
-                       max_seqlen_k=None, scale=None):
-    """Causal varlen prefill: q [sum Lq, Hq, D]; k, v the caches (block_tables given) or packed [sum Lk, Hkv, D]."""
+                       max_seqlen_k=None, scale=None, workspace=None, persistent=None):
+    """Causal varlen prefill: q [sum Lq, Hq, D]; k, v the caches (block_tables given) or packed [sum Lk, Hkv, D].
+
+    bf16: ``persistent=True`` runs the persistent kernel over device-planned work lists in
+    ``workspace`` (allocated here when None); otherwise the one-launch kernel.  The default
+    (None) is persistent exactly when a workspace is passed."""
     torch = _torch()
     _dev(q, "q", ndim=3)
     _dev(out, "out", q.dtype, 3)
@@ -432,12 +444,22 @@ def paged_prefill_attn(q, k, v, cu_seqlens_q, cu_seqlens_k, block_tables, out, m
         max_seqlen_q = int((cq[1:] - cq[:-1]).max()) if B else 0
         max_seqlen_k = int((ck[1:] - ck[:-1]).max()) if B else 0
     sc = 0.0 if scale is None else float(scale)
+    code = _dtype_code(q)
+    if persistent is None:
+        persistent = workspace is not None
+    if not persistent:
+        workspace = None
+    elif workspace is None:
+        need = prefill_workspace_bytes(B, int(max_seqlen_q), Hq, Hkv, D, code)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     if DEBUG_CHECKS:
         _require(check_prefill_inputs(cu_seqlens_q, cu_seqlens_k, block_tables, max_seqlen_q, max_seqlen_k, NB,
                                       bs if block_tables is not None else 1), "paged_prefill_attn")
     _check(lib().pkv_paged_prefill_attn(
         _ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), _ptr(block_tables), W, _ptr(out), sc, B,
-        Tq, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D, NB, bs, _dtype_code(q), _stream()))
+        Tq, int(max_seqlen_q), int(max_seqlen_k), Hq, Hkv, D, NB, bs, code, _ptr(workspace), ws_bytes, _stream()))
     return out
 
 

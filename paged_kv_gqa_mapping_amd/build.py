@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
 
-SOURCES = ["api.cpp", "block_manager.cpp", "copy_kernels.hip", "row_attn.hip", "prefill_mfma.hip", "rope_store.hip", "checks.hip"]
+SOURCES = ["api.cpp", "block_manager.cpp", "copy_kernels.hip", "row_attn.hip", "prefill_mfma.hip", "prefill_plan.hip", "rope_store.hip", "checks.hip"]
 
 # gfx950 only.  Packed fp32 vector instructions are disabled for device code;
 # the host pass does not know the feature and warns, which is harmless.

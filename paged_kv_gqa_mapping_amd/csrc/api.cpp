@@ -522,11 +522,22 @@ int pkv_cascade_decode_attn(const void* q, const void* k_cache, const void* v_ca
   return hip_status(pkv::launch_decode_reduce(r, call.dtype, call.head_dim, s), "decode reduce launch");
 }
 
+int64_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t max_seqlen_q, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t dtype) {
+  if (dtype != PKV_BF16 || num_seqs <= 0 || max_seqlen_q <= 0 || num_kv_heads <= 0 || num_q_heads <= 0 ||
+      num_q_heads % num_kv_heads || (head_dim != 64 && head_dim != 128))
+    return 0;
+  return pkv::prefill_plan_layout(num_seqs, max_seqlen_q, pkv::prefill_head_groups(num_q_heads, num_kv_heads),
+                                  pkv::prefill_tile_positions(num_q_heads, num_kv_heads), head_dim)
+      .total;
+}
+
 int pkv_paged_prefill_attn(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
                            const int32_t* cu_seqlens_k, const int32_t* block_tables, int32_t max_blocks_per_seq,
                            void* out, float scale, int32_t num_seqs, int64_t total_q, int32_t max_seqlen_q,
                            int32_t max_seqlen_k, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                           int64_t num_blocks, int32_t block_size, int32_t dtype, void* stream) {
+                           int64_t num_blocks, int32_t block_size, int32_t dtype, void* workspace,
+                           int64_t workspace_bytes, void* stream) {
   if (num_seqs < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
     return fail(PKV_ERR_INVALID_ARG, "negative size");
   const bool paged = block_tables != nullptr;
@@ -563,6 +574,41 @@ int pkv_paged_prefill_attn(const void* q, const void* k, const void* v, const in
     a.max_blocks_per_seq = max_blocks_per_seq;
     a.log2_block_size = paged ? log2_exact(block_size) : 0;
     a.max_seqlen_q = max_seqlen_q;
+    if (workspace && num_seqs <= pkv::kPlanMaxSeqs) {
+      // persistent kernel over the work lists the plan kernel writes into the workspace
+      const int nhg = pkv::prefill_head_groups(num_q_heads, num_kv_heads);
+      const int qp = pkv::prefill_tile_positions(num_q_heads, num_kv_heads);
+      const pkv::PrefillPlanLayout L = pkv::prefill_plan_layout(num_seqs, max_seqlen_q, nhg, qp, head_dim);
+      if (workspace_bytes < L.total)
+        return fail(PKV_ERR_WORKSPACE, "prefill workspace of %lld bytes needed, %lld given", (long long)L.total,
+                    (long long)workspace_bytes);
+      if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+        return fail(PKV_ERR_INVALID_ARG, "prefill workspace must be 256-byte aligned");
+      uint8_t* w = static_cast<uint8_t*>(workspace);
+      pkv::PrefillPlanArgs p{};
+      p.cu_seqlens_q = cu_seqlens_q;
+      p.cu_seqlens_k = cu_seqlens_k;
+      p.num_seqs = num_seqs;
+      p.nhg = nhg;
+      p.qp = qp;
+      p.items_cap = L.items_cap;
+      p.split_cap = L.split_cap;
+      p.slot_cap = L.slot_cap;
+      p.hdr = reinterpret_cast<int32_t*>(w + L.hdr);
+      p.items = reinterpret_cast<int32_t*>(w + L.items);
+      p.arrive = reinterpret_cast<int32_t*>(w + L.arrive);
+      int st2 = hip_status(pkv::launch_prefill_plan(p, s), "prefill plan launch");
+      if (st2) return st2;
+      a.plan_hdr = p.hdr;
+      a.plan_queue = p.hdr;
+      a.plan_items = p.items;
+      a.plan_arrive = p.arrive;
+      a.plan_states = reinterpret_cast<float*>(w + L.states);
+#ifdef PKV_PREFILL_TIMELINE
+      a.timeline = reinterpret_cast<long long*>(w + L.timeline);
+#endif
+      a.items_cap = L.items_cap;
+    }
     return hip_status(pkv::launch_prefill_mfma(a, head_dim, s), "prefill launch");
   }
   if (!pkv::row_attn_supported(dtype, head_dim, num_q_heads, num_kv_heads))

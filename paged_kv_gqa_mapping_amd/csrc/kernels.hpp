@@ -89,9 +89,107 @@ struct PrefillArgs {
   int32_t num_groups;
   int32_t num_chunks;     // grid: ceil(max shared length / chunk_tokens)
   int32_t member_tiles;   // grid: ceil(max group size / members per workgroup)
+  // Persistent prefill (a workspace was given): the work lists written by
+  // the plan kernel, the per-XCD queue heads, arrival counters of split query
+  // tiles and their softmax-state slots (offsets of PrefillPlanLayout).
+  const int32_t* plan_hdr;
+  int32_t* plan_queue;
+  const int32_t* plan_items;
+  int32_t* plan_arrive;
+  float* plan_states;
+  int32_t items_cap;
+  // built with PKV_PREFILL_TIMELINE only: per workgroup and item, timestamps
+  // of the persistent kernel (a diagnostic; NULL otherwise)
+  long long* timeline;
+};
+// timeline records per workgroup, int64 fields per record
+constexpr int kTimelineItems = 64;
+constexpr int kTimelineFields = 8;
+
+// ---------------------------------------------------------------- persistent prefill plan
+//
+// The persistent prefill runs kPersistWgs workgroups, kPlanCusPerXcd on each
+// of kPlanXcds accelerator dies; workgroup w runs on die w % kPlanXcds and
+// takes work items from that die's list.  An item is one query tile (QP
+// positions x the HW query heads of one KV head) of one sequence and a range
+// of its 128-key tiles.  A query tile with many keys is cut into several
+// items along its keys ("pieces"); each piece writes its unnormalised softmax
+// state, and the last piece to finish merges them.
+constexpr int kPlanXcds = 8;
+constexpr int kPlanCusPerXcd = 32;
+constexpr int kPersistWgs = kPlanXcds * kPlanCusPerXcd;
+// pieces are at least kPlanMinCap key tiles; the cap is chosen so that each
+// die's list holds about kPlanItemsPerCu maximal pieces per workgroup
+#ifndef PKV_PLAN_ITEMS_PER_CU
+#define PKV_PLAN_ITEMS_PER_CU 3
+#endif
+constexpr int kPlanMinCap = 4;
+constexpr int kPlanItemsPerCu = PKV_PLAN_ITEMS_PER_CU;
+constexpr int kPlanThreads = 1024;
+// sequences a plan holds in LDS; a call with more runs the one-launch kernel
+constexpr int kPlanMaxSeqs = 4096;
+// int32 fields of an item record
+constexpr int kItemInts = 8;
+enum ItemField { kItB = 0, kItHg, kItTile, kItKtLo, kItKtHi, kItChunk, kItSplit, kItSlot };  // chunk | nchunks << 16
+// int32 header: queue heads [0, 8), item counts [8, 16), then:
+constexpr int kHdrCap = 16, kHdrOverflow = 17, kHdrSplits = 18, kHdrSlots = 19, kHdrInts = 64;
+
+struct PrefillPlanLayout {
+  int32_t items_cap;  // item records per die
+  int32_t split_cap;  // split query tiles (arrival counters)
+  int32_t slot_cap;   // softmax-state slots
+  int64_t state_floats;  // floats per slot
+  int64_t hdr, items, arrive, states, timeline, total;  // byte offsets, total bytes
 };
 
-// bf16 matrix-core prefill.
+__host__ __device__ inline int64_t plan_align(int64_t x) { return (x + 255) & ~(int64_t)255; }
+
+// qp: query positions per tile; nhg: head groups (query heads / heads per tile).
+__host__ __device__ inline PrefillPlanLayout prefill_plan_layout(int32_t num_seqs, int32_t max_seqlen_q, int32_t nhg,
+                                                                 int32_t qp, int32_t head_dim) {
+  PrefillPlanLayout L{};
+  const int64_t pairs_per_die = ((int64_t)num_seqs * nhg + kPlanXcds - 1) / kPlanXcds;
+  const int64_t tiles_q = ((int64_t)max_seqlen_q + qp - 1) / qp;
+  // every piece beyond a query tile's first is at least `cap` key tiles, and
+  // cap >= (a die's key tiles) / (kPlanItemsPerCu * kPlanCusPerXcd)
+  const int64_t extra = (int64_t)kPlanItemsPerCu * kPlanCusPerXcd;
+  L.items_cap = (int32_t)(pairs_per_die * tiles_q + extra + 8);
+  L.split_cap = (int32_t)(extra * kPlanXcds);
+  L.slot_cap = 2 * L.split_cap;
+  L.state_floats = (int64_t)8 * (head_dim / 32 * 16 + 2) * 64;  // 8 waves x (accumulators + m + l) x 64 lanes
+  int64_t off = 0;
+  L.hdr = off;     off = plan_align(off + kHdrInts * 4);
+  L.items = off;   off = plan_align(off + (int64_t)kPlanXcds * L.items_cap * kItemInts * 4);
+  L.arrive = off;  off = plan_align(off + (int64_t)L.split_cap * 4);
+  L.states = off;  off = plan_align(off + (int64_t)L.slot_cap * L.state_floats * 4);
+#ifdef PKV_PREFILL_TIMELINE
+  L.timeline = off; off = plan_align(off + (int64_t)kPersistWgs * kTimelineItems * kTimelineFields * 8);
+#endif
+  L.total = off;
+  return L;
+}
+
+struct PrefillPlanArgs {
+  const int32_t* cu_seqlens_q;
+  const int32_t* cu_seqlens_k;
+  int32_t num_seqs;
+  int32_t nhg;
+  int32_t qp;
+  int32_t items_cap;
+  int32_t split_cap;
+  int32_t slot_cap;
+  int32_t* hdr;
+  int32_t* items;
+  int32_t* arrive;
+};
+
+hipError_t launch_prefill_plan(const PrefillPlanArgs& p, hipStream_t stream);
+// Query positions per tile and head groups of the matrix-core prefill for these heads.
+int prefill_tile_positions(int32_t num_q_heads, int32_t num_kv_heads);
+int prefill_head_groups(int32_t num_q_heads, int32_t num_kv_heads);
+
+// bf16 matrix-core prefill: one workgroup per query tile (plan_hdr NULL), or the
+// persistent kernel over the plan's work lists (after launch_prefill_plan).
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int32_t head_dim, hipStream_t stream);
 
 // bf16 matrix-core group pass of shared-prefix decode (same kernel, gathered queries).

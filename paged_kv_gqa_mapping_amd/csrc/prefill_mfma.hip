@@ -44,6 +44,17 @@
 // o) written to the member's decode workspace, merged later with the states
 // of its own keys.  The shared keys are thus read once per group instead of
 // once per member.
+//
+// PERSIST mode is the persistent prefill: kPersistWgs workgroups, each on
+// die blockIdx % 8, take items (a query tile and a range of its key tiles)
+// from that die's list, written by the plan kernel (prefill_plan.hip); the
+// first item of a workgroup is given by its index, the next one is claimed
+// from the die's queue head while the current one runs.  An item that is a
+// whole query tile writes the output; a piece of a split query tile writes
+// its unnormalised state (m, l, o) to its slot, counts itself in the tile's
+// arrival counter, and the piece that arrives last merges the states of all
+// pieces in piece order (so the bits do not depend on which piece was last)
+// with M = max m_j, out = sum 2^(m_j - M) o_j / sum 2^(m_j - M) l_j.
 #include <type_traits>
 
 #include "common.hpp"
@@ -130,8 +141,113 @@ __device__ __forceinline__ void wait_vmem() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int D, int HW, bool SHARED>
-__global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a) {
+enum Mode { kGrid = 0, kShared = 1, kPersist = 2 };
+
+// One work item of a workgroup.  Prefill: query tile `tile` of sequence b
+// (Lq queries from packed row q0, Lk keys from packed row k0), key tiles
+// [kt_lo, kt_hi) (kt_hi < 0: all it needs).  Shared: member tile `tile` of a
+// group (Lq members from member0), keys [key_base, key_base + Lk) of its
+// prefix, table row b.  Persistent pieces: piece `piece` of `pieces`, arrival
+// counter `split` (< 0: a whole query tile), state slots from `slot`.
+struct Item {
+  int b, hg, tile, q0, Lq, k0, Lk, key_base, member0, chunk;
+  int kt_lo, kt_hi, piece, pieces, split, slot;
+  long long* tl;  // timeline record of this item (PKV_PREFILL_TIMELINE builds), or NULL
+};
+
+// timeline stamp (a diagnostic of the persistent kernel; compiled out by default)
+__device__ __forceinline__ void stamp(const Item& it, int field) {
+#ifdef PKV_PREFILL_TIMELINE
+  if (it.tl && threadIdx.x == 0) it.tl[field] = wall_clock64();
+#else
+  (void)it;
+  (void)field;
+#endif
+}
+
+// A piece of a split query tile: write this piece's state (per wave and
+// lane: the O^T accumulators, the reference max m and the column's weight
+// sum l) to its slot, count the piece in the tile's arrival counter, and if
+// it is the last to arrive, merge every piece's state in piece order and
+// write the output rows.
+//
+// All pieces of a query tile sit in one die's list, and list x is worked by
+// the workgroups w with w % 8 == x, which the dispatcher places on one die
+// (round-robin over the dies of the partition: die w % 8 on a full chip, as
+// read back from the die id register of every workgroup), so the states,
+// the counter and the merger share one L2 and need no device-wide cache
+// maintenance: each wave waits until its state
+// stores are acknowledged by the L2 (the vector L1 writes through) before
+// the workgroup barrier, the count is an L2 atomic, and the merger's loads
+// miss its L1 (a slot is written once per launch and read once, by the
+// merger; the L1 is invalidated when a launch starts).
+template <int D>
+__device__ __forceinline__ void merge_pieces(const PrefillArgs& a, uint8_t* lds, const Item& it,
+                                             const f32x16_t* acc, float m, float l, bool valid, int64_t q_row) {
+  constexpr int MD = D / 32;
+  constexpr int NR = MD * 16 + 2;  // floats per lane of a wave's state
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int64_t slot_floats = (int64_t)kWaves * NR * 64;
+  float* const wbase = a.plan_states + (int64_t)it.slot * slot_floats + (int64_t)wave * NR * 64 + lane;
+  auto at = [&](int piece, int r) { return wbase + piece * slot_floats + r * 64; };
+#pragma unroll
+  for (int md = 0; md < MD; ++md)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) *at(it.piece, md * 16 + r) = acc[md][r];
+  *at(it.piece, MD * 16) = m;
+  *at(it.piece, MD * 16 + 1) = l;
+  wait_vmem<0>();
+  __syncthreads();
+  volatile int32_t* flag = reinterpret_cast<volatile int32_t*>(lds);
+  if (tid == 0)
+    *flag = __hip_atomic_fetch_add(a.plan_arrive + it.split, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            it.pieces - 1;
+  __syncthreads();
+  if (!*flag) return;
+  if (!valid) return;
+  // M = max_j m_j; L = sum_j 2^(m_j - M) l_j; out = sum_j 2^(m_j - M) o_j / L, in piece order
+  float M = kNegInf;
+  for (int j = 0; j < it.pieces; ++j) M = fmaxf(M, j == it.piece ? m : *at(j, MD * 16));
+  float L = 0.f;
+  for (int j = 0; j < it.pieces; ++j) {
+    const float mj = j == it.piece ? m : *at(j, MD * 16);
+    const float lj = j == it.piece ? l : *at(j, MD * 16 + 1);
+    L = fmaf(exp2_hw(mj - M), lj, L);
+  }
+  const float inv = 1.0f / L;
+  const int half = lane >> 5;
+  uint16_t* op = (uint16_t*)a.out + q_row * D + half * 4;
+#pragma unroll
+  for (int md = 0; md < MD; ++md) {
+    float o[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[r] = 0.f;
+    for (int j = 0; j < it.pieces; ++j) {
+      const float w = exp2_hw((j == it.piece ? m : *at(j, MD * 16)) - M);
+      if (j == it.piece) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[r] = fmaf(w, acc[md][r], o[r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[r] = fmaf(w, *at(j, md * 16 + r), o[r]);
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int r = rr * 4;
+      uint2 w;
+      w.x = pack_bf16x2(o[r] * inv, o[r + 1] * inv);
+      w.y = pack_bf16x2(o[r + 2] * inv, o[r + 3] * inv);
+      *reinterpret_cast<uint2*>(op + md * 32 + rr * 8) = w;
+    }
+  }
+}
+
+template <int D, int HW, int MODE>
+__device__ __forceinline__ void run_item(const PrefillArgs& a, uint8_t* lds, const Item& it) {
+  constexpr bool SHARED = MODE == kShared;
   constexpr int QP = 32 * (kCB / HW);  // positions (members) per workgroup
   constexpr int KSTEPS = D / 16;       // contraction steps of Q K^T
   constexpr int MD = D / 32;           // 32-row blocks of O^T
@@ -141,8 +257,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
   constexpr int RPI = 1024 / ROWB;     // rows per copy instruction (4 or 8)
   constexpr int RW = kKT / kWaves;     // rows of each tile copied by one wave
   constexpr int IPW = RW / RPI;        // copy instructions per wave, tile and tensor
-  // K tile buffers, then V tile buffers (160 KiB for D = 128 with the skew)
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[(kKBufs + kVBufs) * TILEB];
 
   const int tid = threadIdx.x;
   // wave-uniform (scalar): the tile loop bounds and the block-id lookups derive from it
@@ -153,52 +267,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
   const int Hq = a.num_q_heads;
   const int Hkv = a.num_kv_heads;
   const int G = Hq / Hkv;
-  const int NHG = Hq / HW;
-
-  int id = blockIdx.x;
-  int hg;
-  if constexpr (SHARED) {
-    hg = id % NHG;
-    id /= NHG;
-  }
-  // Prefill: sequence b, its query tile `tile` (Lq queries, Lk keys, packed
-  // rows from k0).  Shared: group member tile `tile` (Lq members), keys
-  // [key_base, key_base + Lk) of the prefix, table row of the group's first
-  // member b.
-  int b, tile, q0 = 0, Lq, k0 = 0, Lk, key_base = 0, member0 = 0, chunk = 0;
-  if constexpr (SHARED) {
-    tile = id % a.member_tiles;
-    id /= a.member_tiles;
-    chunk = id % a.num_chunks;
-    const int gi = id / a.num_chunks;
-    member0 = a.group_offsets[gi];
-    Lq = a.group_offsets[gi + 1] - member0;
-    if (tile * QP >= Lq) return;
-    b = a.group_seqs[member0];
-    const int shared = a.shared_lens[b];
-    key_base = chunk * a.chunk_tokens;
-    if (key_base >= shared) return;
-    Lk = min(shared - key_base, a.chunk_tokens);
-  } else {
-    // Workgroups are dispatched to the 8 XCDs round-robin (block B on XCD
-    // B % 8), each XCD with its own L2.  The query tiles of one (sequence, head
-    // group) pair are placed on one XCD at consecutive slots, so the workgroups
-    // that run there together read the same K/V tiles through that L2.
-    const int xcd = id % kXcds;
-    const int slot = id / kXcds;
-    const int pair = (slot / a.tiles_per_pair) * kXcds + xcd;
-    if (pair >= a.num_seqs * NHG) return;
-    const int tile_rev = slot % a.tiles_per_pair;
-    hg = pair % NHG;
-    b = pair / NHG;
-    q0 = a.cu_seqlens_q[b];
-    Lq = a.cu_seqlens_q[b + 1] - q0;
-    k0 = a.cu_seqlens_k[b];
-    Lk = a.cu_seqlens_k[b + 1] - k0;
-    const int n_qt = (Lq + QP - 1) / QP;
-    tile = n_qt - 1 - tile_rev;  // tiles with the most keys are dispatched first
-    if (tile < 0) return;
-  }
+  const int b = it.b, hg = it.hg, tile = it.tile, q0 = it.q0, Lq = it.Lq, k0 = it.k0, Lk = it.Lk;
+  const int key_base = it.key_base, member0 = it.member0, chunk = it.chunk;
   const int g = (hg * HW) / G;
   // Positions are relative to key_base.  Prefill: query i sits at shift + i.
   // Shared: every column sees the whole chunk, as a query at its last key.
@@ -226,8 +296,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
     }
   }
   const int wg_max_pos = SHARED ? Lk - 1 : shift + min(tile * QP + QP, Lq) - 1;
-  const int n_kt = wg_max_pos / kKT + 1;
-  const int n_kt_wave = w_max_pos >= 0 ? min(n_kt, w_max_pos / kKT + 1) : 0;
+  // key tiles [kt_lo, n_kt) of this item; this wave computes [kt_lo, n_kt_wave)
+  const int kt_lo = it.kt_lo;
+  const int n_kt = it.kt_hi >= 0 ? it.kt_hi : wg_max_pos / kKT + 1;
+  const int n_kt_wave = w_max_pos >= 0 ? min(n_kt, w_max_pos / kKT + 1) : kt_lo;
 
   // Tile copies.  Wave w copies rows RW w .. RW w + RW - 1 of each K and V tile
   // (IPW instructions each, RPI rows per instruction); lane L of an
@@ -487,9 +559,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
       qf[nb][kk] = __builtin_bit_cast(bf16x8_t, x);
     }
   }
-  fetch_blocks(0);
-  issue_copies(0, 0);
-  if (n_kt > 1) fetch_blocks(1);
+  fetch_blocks(kt_lo);
+  issue_copies(kt_lo, 0);
+  if (kt_lo + 1 < n_kt) fetch_blocks(kt_lo + 1);
 
   // The compiler's own wait for these loads happens here, once: inside the
   // loop it would also wait for every tile copy in flight.
@@ -508,12 +580,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
   auto tile_loop = [&](auto LATE) __attribute__((always_inline)) {
     constexpr bool is_late = decltype(LATE)::value;
     int vprev = kVBufs - 1, vcur = 0, vnext = 1 % kVBufs;
-    for (int kt = 0; kt < n_kt; ++kt) {
+    for (int kt = kt_lo; kt < n_kt; ++kt) {
       wait_vmem<0>();
       __syncthreads();
+      if (kt == kt_lo) stamp(it, 5);
       if (kt + 1 < n_kt) issue_copies(kt + 1, vnext);
       if constexpr (is_late) {
-        if (kt >= 1 && kt <= n_kt_wave) pv(vprev, std::false_type{});
+        if (kt >= kt_lo + 1 && kt <= n_kt_wave) pv(vprev, std::false_type{});
         if (kt < n_kt_wave) qk_softmax(kt & 1, kt * kKT, 0, std::false_type{});
       } else {
         if (kt < n_kt_wave) {
@@ -530,14 +603,22 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
     }
     // a late wave's last tile (no copies are in flight any more)
     if constexpr (is_late)
-      if (n_kt_wave == n_kt && n_kt > 0) pv(vprev, std::false_type{});
+      if (n_kt_wave == n_kt && n_kt > kt_lo) pv(vprev, std::false_type{});
   };
   if (kSkew && wave >= kWaves / 2)
     tile_loop(std::true_type{});
   else
     tile_loop(std::false_type{});
 
-  if (n_kt_wave == 0) return;
+  stamp(it, 6);
+  if constexpr (MODE == kPersist) {
+    if (it.split >= 0) {
+      merge_pieces<D>(a, lds, it, acc_o[0], m[0], halves_sum(lsum[0]), col_valid[0] && n_kt_wave > kt_lo,
+                      q_row[0]);
+      return;
+    }
+  }
+  if (n_kt_wave == kt_lo) return;
   if constexpr (SHARED) {
     // unnormalised state of each column at slot slot0 + chunk of its member's pair
 #pragma unroll
@@ -581,20 +662,133 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
   }
 }
 
+template <int D, int HW, int MODE>
+__global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a) {
+  constexpr int QP = 32 * (kCB / HW);
+  // K tile buffers, then V tile buffers (160 KiB for D = 128 with the skew)
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[(kKBufs + kVBufs) * kKT * 2 * D];
+  const int NHG = a.num_q_heads / HW;
+  if constexpr (MODE == kShared) {
+    Item it{};
+    it.kt_hi = -1;
+    it.split = -1;
+    int id = blockIdx.x;
+    it.hg = id % NHG;
+    id /= NHG;
+    it.tile = id % a.member_tiles;
+    id /= a.member_tiles;
+    it.chunk = id % a.num_chunks;
+    const int gi = id / a.num_chunks;
+    it.member0 = a.group_offsets[gi];
+    it.Lq = a.group_offsets[gi + 1] - it.member0;
+    if (it.tile * QP >= it.Lq) return;
+    it.b = a.group_seqs[it.member0];
+    const int shared = a.shared_lens[it.b];
+    it.key_base = it.chunk * a.chunk_tokens;
+    if (it.key_base >= shared) return;
+    it.Lk = min(shared - it.key_base, a.chunk_tokens);
+    run_item<D, HW, MODE>(a, lds, it);
+  } else if constexpr (MODE == kGrid) {
+    // Workgroups are dispatched to the 8 XCDs round-robin (block B on XCD
+    // B % 8), each XCD with its own L2.  The query tiles of one (sequence, head
+    // group) pair are placed on one XCD at consecutive slots, so the workgroups
+    // that run there together read the same K/V tiles through that L2.
+    Item it{};
+    it.kt_hi = -1;
+    it.split = -1;
+    const int id = blockIdx.x;
+    const int xcd = id % kXcds;
+    const int slot = id / kXcds;
+    const int pair = (slot / a.tiles_per_pair) * kXcds + xcd;
+    if (pair >= a.num_seqs * NHG) return;
+    const int tile_rev = slot % a.tiles_per_pair;
+    it.hg = pair % NHG;
+    it.b = pair / NHG;
+    it.q0 = a.cu_seqlens_q[it.b];
+    it.Lq = a.cu_seqlens_q[it.b + 1] - it.q0;
+    it.k0 = a.cu_seqlens_k[it.b];
+    it.Lk = a.cu_seqlens_k[it.b + 1] - it.k0;
+    const int n_qt = (it.Lq + QP - 1) / QP;
+    it.tile = n_qt - 1 - tile_rev;  // tiles with the most keys are dispatched first
+    if (it.tile < 0) return;
+    run_item<D, HW, MODE>(a, lds, it);
+  } else {
+    // the die's list; the first item by workgroup index, the next ones from the
+    // die's queue head (claimed at the start of the current item)
+    const int xcd = blockIdx.x % kPlanXcds;
+    const_i32_t* hdr = (const_i32_t*)a.plan_hdr;
+    const int count = min(hdr[kPlanXcds + xcd], a.items_cap);
+    int idx = blockIdx.x / kPlanXcds;
+#ifdef PKV_PREFILL_TIMELINE
+    int n_items = 0;
+    long long t_item = wall_clock64();
+#endif
+    while (idx < count) {
+      int next = 0;
+      if (threadIdx.x == 0)
+        next = __hip_atomic_fetch_add(a.plan_queue + xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const_i32_t* rec = (const_i32_t*)a.plan_items + ((int64_t)xcd * a.items_cap + idx) * kItemInts;
+      Item it{};
+      it.b = rec[kItB];
+      it.hg = rec[kItHg];
+      it.tile = rec[kItTile];
+      it.kt_lo = rec[kItKtLo];
+      it.kt_hi = rec[kItKtHi];
+      it.piece = rec[kItChunk] & 0xffff;
+      it.pieces = rec[kItChunk] >> 16;
+      it.split = rec[kItSplit];
+      it.slot = rec[kItSlot];
+      const_i32_t* cq = (const_i32_t*)a.cu_seqlens_q;
+      const_i32_t* ck = (const_i32_t*)a.cu_seqlens_k;
+      it.q0 = cq[it.b];
+      it.Lq = cq[it.b + 1] - it.q0;
+      it.k0 = ck[it.b];
+      it.Lk = ck[it.b + 1] - it.k0;
+#ifdef PKV_PREFILL_TIMELINE
+      if (a.timeline && n_items < kTimelineItems) {
+        it.tl = a.timeline + ((int64_t)blockIdx.x * kTimelineItems + n_items) * kTimelineFields;
+        if (threadIdx.x == 0) {
+          it.tl[0] = idx | ((long long)xcd << 32);
+          it.tl[1] = it.b | ((long long)it.hg << 16) | ((long long)it.tile << 32);
+          it.tl[2] = it.kt_lo | ((long long)it.kt_hi << 32);
+          it.tl[3] = it.piece | ((long long)it.pieces << 16) | ((long long)(it.split + 1) << 32);
+          it.tl[4] = t_item;
+        }
+      }
+      ++n_items;
+#endif
+      run_item<D, HW, MODE>(a, lds, it);
+      // every wave is done with the tile buffers before the next item's copies
+      __syncthreads();
+      stamp(it, 7);
+      if (threadIdx.x == 0) *reinterpret_cast<volatile int32_t*>(lds) = next;
+      __syncthreads();
+      idx = uniform(*reinterpret_cast<volatile int32_t*>(lds));
+#ifdef PKV_PREFILL_TIMELINE
+      t_item = wall_clock64();
+#endif
+    }
+#ifdef PKV_PREFILL_TIMELINE
+    if (a.timeline && n_items < kTimelineItems && threadIdx.x == 0)
+      a.timeline[((int64_t)blockIdx.x * kTimelineItems + n_items) * kTimelineFields] = -1;  // end of this list
+#endif
+  }
+}
+
 // Query heads per workgroup: the largest of 8, 4, 2, 1 that divides the group size.
 int heads_per_wg(int32_t num_q_heads, int32_t num_kv_heads) {
   const int G = num_q_heads / num_kv_heads;
   return (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
 }
 
-template <bool SHARED>
+template <int MODE>
 hipError_t launch(const PrefillArgs& a, int32_t head_dim, int64_t blocks, int HW, hipStream_t stream) {
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   dim3 grid((unsigned)blocks), block(kThreads);
 #define PKV_PREFILL_CASE(DD, HH)                                                                     \
   if (head_dim == DD && HW == HH) {                                                                  \
-    hipLaunchKernelGGL((prefill_mfma_kernel<DD, HH, SHARED>), grid, block, 0, stream, a);            \
+    hipLaunchKernelGGL((prefill_mfma_kernel<DD, HH, MODE>), grid, block, 0, stream, a);              \
     return hipGetLastError();                                                                        \
   }
   PKV_PREFILL_CASE(128, 8)
@@ -613,11 +807,20 @@ hipError_t launch(const PrefillArgs& a, int32_t head_dim, int64_t blocks, int HW
 
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int32_t head_dim, hipStream_t stream) {
   const int HW = heads_per_wg(a.num_q_heads, a.num_kv_heads);
+  if (a.plan_hdr) return launch<kPersist>(a, head_dim, kPersistWgs, HW, stream);
   const int QP = 32 * (kCB / HW);
   PrefillArgs b = a;
   b.tiles_per_pair = (a.max_seqlen_q + QP - 1) / QP;
   const int64_t pairs = (int64_t)a.num_seqs * (a.num_q_heads / HW);
-  return launch<false>(b, head_dim, (pairs + kXcds - 1) / kXcds * kXcds * b.tiles_per_pair, HW, stream);
+  return launch<kGrid>(b, head_dim, (pairs + kXcds - 1) / kXcds * kXcds * b.tiles_per_pair, HW, stream);
+}
+
+int prefill_tile_positions(int32_t num_q_heads, int32_t num_kv_heads) {
+  return 32 * (kCB / heads_per_wg(num_q_heads, num_kv_heads));
+}
+
+int prefill_head_groups(int32_t num_q_heads, int32_t num_kv_heads) {
+  return num_q_heads / heads_per_wg(num_q_heads, num_kv_heads);
 }
 
 int shared_prefix_members_per_wg(int32_t num_q_heads, int32_t num_kv_heads) {
@@ -634,7 +837,7 @@ int64_t shared_prefix_wgs_per_chunk(int32_t num_q_heads, int32_t num_kv_heads, i
 hipError_t launch_shared_prefix_mfma(const PrefillArgs& a, int32_t head_dim, hipStream_t stream) {
   const int HW = heads_per_wg(a.num_q_heads, a.num_kv_heads);
   const int64_t blocks = (int64_t)a.num_groups * a.num_chunks * a.member_tiles * (a.num_q_heads / HW);
-  return launch<true>(a, head_dim, blocks, HW, stream);
+  return launch<kShared>(a, head_dim, blocks, HW, stream);
 }
 
 }  // namespace pkv

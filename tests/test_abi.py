@@ -88,9 +88,9 @@ def test_kv_store_and_prefill_argument_errors():
     assert L.pkv_kv_store(P, P, P, P, None, 4, 8, 128, 10, 256, 1, None) == -1
     assert L.pkv_kv_store(P, P, P, P, P, 4, 8, 128, 10, 100, 1, None) == -2
     # prefill: max_seqlen_q > max_seqlen_k, and a table too narrow for max_seqlen_k
-    assert L.pkv_paged_prefill_attn(P, P, P, P, P, P, 4, P, 0.0, 2, 10, 9, 8, 32, 8, 128, 10, 256, 1, None) == -1
-    assert L.pkv_paged_prefill_attn(P, P, P, P, P, P, 1, P, 0.0, 2, 10, 9, 300, 32, 8, 128, 10, 256, 1, None) == -1
-    assert L.pkv_paged_prefill_attn(P, P, P, P, P, P, 4, P, 0.0, 0, 0, 0, 0, 32, 8, 128, 10, 256, 1, None) == 0
+    assert L.pkv_paged_prefill_attn(P, P, P, P, P, P, 4, P, 0.0, 2, 10, 9, 8, 32, 8, 128, 10, 256, 1, None, 0, None) == -1
+    assert L.pkv_paged_prefill_attn(P, P, P, P, P, P, 1, P, 0.0, 2, 10, 9, 300, 32, 8, 128, 10, 256, 1, None, 0, None) == -1
+    assert L.pkv_paged_prefill_attn(P, P, P, P, P, P, 4, P, 0.0, 0, 0, 0, 0, 32, 8, 128, 10, 256, 1, None, 0, None) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):

@@ -65,8 +65,20 @@ def _pools_bitwise(r):
 
 def _oracle_prefill(r):
     w = r.w
-    return oracle.prefill(w.pre_q, r.kc, r.vc, w.cu_seqlens_q, w.cu_seqlens_k, w.pre_block_tables, w.scale, w.dtype,
-                          w.block_size)
+    if getattr(r, "pre_ref", None) is None:
+        r.pre_ref = oracle.prefill(w.pre_q, r.kc, r.vc, w.cu_seqlens_q, w.cu_seqlens_k, w.pre_block_tables, w.scale,
+                                   w.dtype, w.block_size)
+    return r.pre_ref
+
+
+def _one_launch_prefill(r):
+    """The same prefill through the one-launch kernel (no workspace)."""
+    s, w = r.step, r.w
+    out = torch.empty_like(s.pre_out)
+    pkv.paged_prefill_attn(s.pre_q, s.k_cache, s.v_cache, s.cu_q, s.cu_k, s.pre_bt, out, max_seqlen_q=w.max_seqlen_q,
+                           max_seqlen_k=w.max_seqlen_k, scale=w.scale, persistent=False)
+    torch.cuda.synchronize()
+    return out
 
 
 def _with_private_copies(step, tables, rows, shared_ids):
@@ -105,13 +117,20 @@ def test_prefix_cached_prefill_every_row(c4):
     assert err <= tol(w.dtype), err
 
 
+def test_prefix_cached_prefill_one_launch_kernel_same_bits(c4):
+    """No query tile here has more key tiles than the piece cap, so the persistent
+    kernel computes every tile exactly as the one-launch kernel does."""
+    out = _one_launch_prefill(c4)
+    assert torch.equal(out.view(torch.int16), c4.step.pre_out.view(torch.int16))
+
+
 def test_prefix_cached_prefill_shared_equals_private_bitwise(c4):
     w, s = c4.w, c4.step
     rows = list(range(len(w.cu_seqlens_q) - 1))
     k2, v2, t2 = _with_private_copies(s, w.pre_block_tables, rows, w.shared_blocks)
     out2 = torch.empty_like(s.pre_out)
     pkv.paged_prefill_attn(s.pre_q, k2, v2, s.cu_q, s.cu_k, to_dev(t2), out2, max_seqlen_q=w.max_seqlen_q,
-                           max_seqlen_k=w.max_seqlen_k, scale=w.scale)
+                           max_seqlen_k=w.max_seqlen_k, scale=w.scale, persistent=True)
     torch.cuda.synchronize()
     assert torch.equal(out2.view(torch.int16), s.pre_out.view(torch.int16))
 
@@ -142,6 +161,24 @@ def test_mixed_step_prefill_every_row(c5):
     err = max_abs(got, ref, w.dtype)
     log(f"mixed step prefill, all {got.shape[0]} chunk rows: max abs error {err:.3g}")
     assert err <= tol(w.dtype), err
+
+
+def test_mixed_step_prefill_one_launch_kernel_every_row(c5):
+    """The chunks' query tiles are cut into pieces by the persistent kernel; the
+    one-launch kernel computes them whole.  Both against the oracle."""
+    w = c5.w
+    got = to_host(_one_launch_prefill(c5), w.dtype)
+    err = max_abs(got, _oracle_prefill(c5), w.dtype)
+    log(f"mixed step prefill, one-launch kernel, all rows: max abs error {err:.3g}")
+    assert err <= tol(w.dtype), err
+
+
+def test_mixed_step_prefill_repeats_bitwise(c5):
+    s = c5.step
+    first = s.pre_out.clone()
+    s.prefill()
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int16), s.pre_out.view(torch.int16))
 
 
 def test_mixed_step_decode_shared_equals_private_bitwise(c5):

@@ -86,18 +86,40 @@ PREFILL_SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("persistent", [True, False], ids=["persistent", "one-launch"])
 @pytest.mark.parametrize("shape", PREFILL_SHAPES, ids=lambda s: "-".join(map(str, s)))
-def test_prefill_tiny_sweep(shape):
+def test_prefill_tiny_sweep(shape, persistent):
+    """With the persistent kernel the pairs (3, 1500) and (64, 1100) are cut into
+    pieces of 4 key tiles (the smallest cap), so the piece merge is covered."""
     dtype, hq, hkv, d, bs = shape
     w = _prefill_case(dtype, hq, hkv, d, bs, PREFILL_PAIRS, seed=hq * 3 + bs)
-    log(f"prefill sweep {shape}")
+    log(f"prefill sweep {shape} persistent={persistent}")
     step = DeviceStep(w)
-    step.step()
+    step.step(persistent=persistent)
     kc, vc = _check_store(step, w)
     ref = oracle.prefill(w.pre_q, kc, vc, w.cu_seqlens_q, w.cu_seqlens_k, w.pre_block_tables, w.scale, dtype,
                          w.block_size)
     err = max_abs(to_host(step.pre_out, dtype), ref, dtype)
     assert err <= tol(dtype), f"max abs error {err}"
+
+
+def test_prefill_persistent_repeats_bitwise_and_rejects_small_workspace():
+    """The last piece to arrive merges all pieces in piece order, so repeated
+    calls give the same bits whichever piece finishes last."""
+    w = _prefill_case("bf16", 32, 8, 128, 16, [(3, 1500), (64, 1100), (200, 700), (700, 3000)], seed=21)
+    step = DeviceStep(w)
+    step.step()
+    first = step.pre_out.clone()
+    for _ in range(3):
+        step.prefill()
+        torch.cuda.synchronize()
+        assert torch.equal(first.view(torch.int16), step.pre_out.view(torch.int16))
+    need = pkv.prefill_workspace_bytes(4, w.max_seqlen_q, 32, 8, 128, 1)
+    small = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(pkv.PkvError, match="workspace"):
+        pkv.paged_prefill_attn(step.pre_q, step.k_cache, step.v_cache, step.cu_q, step.cu_k, step.pre_bt,
+                               step.pre_out, max_seqlen_q=w.max_seqlen_q, max_seqlen_k=w.max_seqlen_k,
+                               scale=w.scale, workspace=small)
 
 
 # packed k/v (no block table): group sizes 1-8, both head dims; the last pair walks 12 key tiles
