@@ -22,6 +22,31 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+
+def _pin_blas_threads() -> int:
+    """BLAS / OpenMP threads of the oracle = the cores this process may run on (or a
+    smaller cap the environment already sets), fixed before numpy is first imported."""
+    n = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ.setdefault(var, str(n))
+    return n
+
+
+BLAS_THREADS = _pin_blas_threads()
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_split_traffic.md")
@@ -92,33 +117,75 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, kc, vc, budget_s: float = 12.0):
-    """The fp64 oracle timed on a bounded sample of the decode part of the workload:
-    whole sequences, in order, until the time budget is spent.  Returns KV GB/s."""
+def cpu_baseline(w, decode_budget_s: float = 12.0, prefill_budget_s: float = 6.0):
+    """The fp64 oracle, as it stands, timed on the host on bounded samples of the same
+    workload, with the GPU figures' algorithmic numerators:
+
+    * kv_store: the whole step's new tokens (the oracle returns new caches, so its time
+      includes copying the pool; GB/s over the store's algorithmic bytes);
+    * decode (the metric): whole sequences in order until the budget is spent, KV GB/s;
+    * prefill: query rows of the chunks, the longest sequence first, until the budget is
+      spent, TFLOP/s over 4 * Hq * D per (query, key) pair.
+
+    Returns the cpu_baseline record (value = decode GB/s) and the caches after the store."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     import oracle
 
     t0 = time.perf_counter()
+    kc, vc = oracle.kv_store(w.k_cache, w.v_cache, w.new_k, w.new_v, w.slot_mapping, w.block_size)
+    t_store = time.perf_counter() - t0
+
+    t0 = time.perf_counter()
     done_bytes = 0
     n = 0
     row = 2 * w.num_kv_heads * w.head_dim * w.elt_bytes
-    while n < len(w.dec_context_lens) and time.perf_counter() - t0 < budget_s:
+    while n < len(w.dec_context_lens) and time.perf_counter() - t0 < decode_budget_s:
         oracle.decode(w.dec_q[n:n + 1], kc, vc, w.dec_block_tables[n:n + 1], w.dec_context_lens[n:n + 1], w.scale,
                       w.dtype, w.block_size)
         done_bytes += int(w.dec_context_lens[n]) * row
         n += 1
-    dt = time.perf_counter() - t0
+    t_dec = time.perf_counter() - t0
+
+    pre = None
+    if w.pre_q is not None:
+        lq = np.diff(w.cu_seqlens_q)
+        lk = np.diff(w.cu_seqlens_k)
+        s = int(np.argmax(lk))
+        q0, Lq, Lk = int(w.cu_seqlens_q[s]), int(lq[s]), int(lk[s])
+        t0 = time.perf_counter()
+        pairs = rows = 0
+        for i in range(Lq - 1, -1, -1):
+            if time.perf_counter() - t0 >= prefill_budget_s:
+                break
+            p = Lk - Lq + i
+            oracle.prefill(w.pre_q[q0 + i:q0 + i + 1], kc, vc, np.array([0, 1], np.int32),
+                           np.array([0, p + 1], np.int32), w.pre_block_tables[s:s + 1], w.scale, w.dtype,
+                           w.block_size)
+            pairs += p + 1
+            rows += 1
+        t_pre = time.perf_counter() - t0
+        pre = {"TFLOP/s": round(4 * w.num_q_heads * w.head_dim * pairs / t_pre / 1e12, 6), "rows": rows,
+               "seconds": round(t_pre, 2)}
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {
-        "value": round(done_bytes / dt / 1e9, 4),
+    rec = {
+        "value": round(done_bytes / t_dec / 1e9, 4),
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"fp64 numpy oracle decode of the first {n} of {len(w.dec_context_lens)} decode sequences "
-                  f"({done_bytes / 1e9:.3f} GB of K/V, {dt:.1f} s), same algorithmic bytes per token as the GPU figure",
+        "cpu": cpu_model(),
+        "sample": f"fp64 numpy oracle on the host: decode of the first {n} of {len(w.dec_context_lens)} decode "
+                  f"sequences ({done_bytes / 1e9:.3f} GB of K/V, {t_dec:.1f} s; value, same algorithmic bytes per "
+                  f"token as the GPU figure)"
+                  + (f"; prefill of {pre['rows']} query rows of the longest chunk ({pre['seconds']} s)" if pre else "")
+                  + f"; kv_store of all {len(w.slot_mapping)} new tokens ({t_store:.1f} s, includes copying the pool)",
+        "kv_store_GB/s": round(w.store_bytes() / t_store / 1e9, 6),
+        "decode_GB/s": round(done_bytes / t_dec / 1e9, 4),
     }
+    if pre:
+        rec["prefill_TFLOP/s"] = pre["TFLOP/s"]
+    return rec
 
 
 def measure_rope_kv_store(w, torch, pkv, dev, pq, dq, nk, nv, kc, vc, slots, bf, iters=20):
@@ -293,6 +360,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=5, help="workload number (5 = the mixed step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="no cache-evicting read between timed steps (ms_per_step is then still the step events' mean)")
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the separately timed next-row measurements (fused rope + kv_store, cascade decode)")
@@ -391,7 +460,7 @@ def main():
     if args.fused_store and (not has_dec or args.cascade):
         print("--fused-store needs decode sequences and plain decode", file=sys.stderr)
         sys.exit(2)
-    n_ev = 7
+    n_ev = 8
     overlap = args.overlap_prefill and has_pre and has_dec
     s_pre = torch.cuda.Stream() if overlap else None
 
@@ -433,6 +502,7 @@ def main():
         rec(4)
         if overlap:
             torch.cuda.current_stream().wait_stream(s_pre)
+        rec(7)  # end of the step (after prefill too, when it ran on its own stream)
 
     if args.graph:
         # capture once (after a warm-up on the capture stream), then time replays
@@ -454,17 +524,28 @@ def main():
         ms = (time.perf_counter() - t0) * 1e3 / args.steps
         print(json.dumps({"workload": w.name, "graph_ms_per_step": round(ms, 5), "steps": args.steps}), flush=True)
         return
+    # between timed steps a 512 MiB read (twice the last-level cache) evicts what the
+    # previous step left in the caches; it is outside the step's events, so
+    # ms_per_step is the mean event time of the steps themselves
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def evict():
+        if flush is not None:
+            flush.view(torch.int32).sum()
+
     for _ in range(args.warmup):
+        evict()
         step()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
+        evict()
         step(evs[k])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = float(np.mean([e[0].elapsed_time(e[7]) for e in evs]))
 
     def avg(i, j):
         return float(np.mean([e[i].elapsed_time(e[j]) for e in evs]))  # ms
@@ -513,10 +594,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and has_dec:
         log("timing the oracle on a bounded sample")
-        import oracle
-
-        okc, ovc = oracle.kv_store(w.k_cache, w.v_cache, w.new_k, w.new_v, w.slot_mapping, w.block_size)
-        cpu = cpu_baseline(w, okc, ovc)
+        cpu = cpu_baseline(w)
 
     out = {
         "metric": "paged decode attn KV GB/s & % HBM peak; prefill attn TFLOP/s & % MFMA peak",
@@ -526,6 +604,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "wall_ms_per_step_incl_eviction": round(wall * 1e3 / args.steps, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -380,12 +380,14 @@ int pkv_paged_gather(const void* k_cache, const void* v_cache, const int32_t* bl
  * - A full block written by one sequence only (count 1) is registered in the
  *   cache; freed blocks (count 0) keep their registration and stay reusable
  *   until the block is handed out again for new data (free blocks are reused
- *   oldest first).  A sequence's partial last block is always its own.
+ *   oldest first, and a sequence's blocks are freed last block first, so its
+ *   prefix stays cached longest).  A sequence's partial last block is always
+ *   its own.
  * - Slots are int32: num_blocks * block_size must be below 2^31.
  * - Each manager is internally locked; calls on one manager may come from
  *   several threads.  Errors return a negative pkv_status with text in
  *   pkv_bm_last_error() (thread-local); PKV_ERR_OUT_OF_BLOCKS leaves the
- *   manager unchanged, so a caller can preempt and retry.
+ *   manager unchanged, so a caller can preempt (pkv_bm_preempt) and retry.
  */
 typedef struct pkv_block_manager pkv_block_manager;
 
@@ -415,6 +417,18 @@ int pkv_bm_append(pkv_block_manager* bm, int64_t seq_id, int32_t token, int32_t*
 
 /* Release a sequence's blocks. */
 int pkv_bm_free(pkv_block_manager* bm, int64_t seq_id);
+
+/* Preemption when the pool runs short (nano-vLLM's scheduler evicts running
+ * sequences back to its waiting queue and frees their blocks when the KV
+ * cache is exhausted: "Nano-vLLM Architecture and Performance", section "Key
+ * Features", item "Preemption").  Frees the blocks of the most recently
+ * allocated sequence still held and forgets it; the caller keeps its tokens
+ * and re-queues it.  *seq_id (may be NULL) receives its id; *num_cached_tokens
+ * (may be NULL) receives how many of its leading tokens the prefix cache
+ * still holds right after the free (what re-allocating it would reuse if no
+ * other allocation takes those blocks first).  PKV_ERR_INVALID_ARG if no
+ * sequence holds blocks. */
+int pkv_bm_preempt(pkv_block_manager* bm, int64_t* seq_id, int64_t* num_cached_tokens);
 
 /* Tokens of a sequence (its context length), or a negative status. */
 int64_t pkv_bm_seq_len(pkv_block_manager* bm, int64_t seq_id);

@@ -147,6 +147,8 @@ def lib() -> ctypes.CDLL:
     L.pkv_bm_append.restype = ctypes.c_int
     L.pkv_bm_free.argtypes = [P, I64]
     L.pkv_bm_free.restype = ctypes.c_int
+    L.pkv_bm_preempt.argtypes = [P, ctypes.POINTER(I64), ctypes.POINTER(I64)]
+    L.pkv_bm_preempt.restype = ctypes.c_int
     L.pkv_bm_seq_len.argtypes = [P, I64]
     L.pkv_bm_seq_len.restype = I64
     L.pkv_bm_block_table.argtypes = [P, I64, P, I32, I32]
@@ -630,6 +632,13 @@ class BlockManager:
 
     def free(self, seq_id: int) -> None:
         self._check(lib().pkv_bm_free(self._h, int(seq_id)))
+
+    def preempt(self):
+        """Free the most recently allocated sequence; returns (seq_id, cached_tokens), the
+        second being how many of its leading tokens the prefix cache still holds."""
+        sid, cached = ctypes.c_int64(0), ctypes.c_int64(0)
+        self._check(lib().pkv_bm_preempt(self._h, ctypes.byref(sid), ctypes.byref(cached)))
+        return int(sid.value), int(cached.value)
 
     def seq_len(self, seq_id: int) -> int:
         return int(self._check(lib().pkv_bm_seq_len(self._h, int(seq_id))))

@@ -51,6 +51,7 @@ struct Seq {
   std::vector<int32_t> tokens;  // every token id of the sequence
   uint64_t last_full_hash = 0;  // hash of the last full block (0 before the first)
   int64_t cached_tokens = 0;    // prompt tokens found in the prefix cache at allocation
+  uint64_t order = 0;           // allocation order (preemption takes the most recent)
 };
 
 }  // namespace
@@ -70,6 +71,7 @@ struct pkv_block_manager {
   int64_t num_free = 0;
   std::unordered_map<uint64_t, int32_t> cache;  // hash -> block
   std::unordered_map<int64_t, Seq> seqs;
+  uint64_t next_order = 0;
   std::mutex mu;
 
   void push_back(int32_t b) {
@@ -102,6 +104,11 @@ struct pkv_block_manager {
   }
   void release(int32_t b) {
     if (--ref[b] == 0) push_back(b);
+  }
+  // a sequence's blocks, last first: its prefix blocks enter the free list last
+  // and so keep their cache registration longest (they are the most reusable)
+  void release_all(const std::vector<int32_t>& blocks) {
+    for (auto it = blocks.rbegin(); it != blocks.rend(); ++it) release(*it);
   }
   // a cached block for this (hash, tokens), or -1
   int32_t lookup(uint64_t h, const int32_t* tokens) const {
@@ -231,6 +238,7 @@ int pkv_bm_allocate(pkv_block_manager* m, int64_t seq_id, const int32_t* tokens,
     if (full) s.last_full_hash = h;
   }
   s.tokens.assign(tokens, tokens + num_tokens);
+  s.order = m->next_order++;
   if (num_cached_tokens) *num_cached_tokens = s.cached_tokens;
   m->seqs.emplace(seq_id, std::move(s));
   return PKV_OK;
@@ -262,8 +270,36 @@ int pkv_bm_free(pkv_block_manager* m, int64_t seq_id) {
   std::lock_guard<std::mutex> g(m->mu);
   auto it = m->seqs.find(seq_id);
   if (it == m->seqs.end()) return bm_fail(PKV_ERR_INVALID_ARG, "unknown sequence %lld", (long long)seq_id);
-  for (int32_t b : it->second.blocks) m->release(b);
+  m->release_all(it->second.blocks);
   m->seqs.erase(it);
+  return PKV_OK;
+}
+
+// Leading tokens of a token array that the prefix cache holds (whole blocks,
+// up to the first miss).
+static int64_t cached_prefix(pkv_block_manager* m, const int32_t* tokens, int64_t n) {
+  if (!m->prefix_cache) return 0;
+  const int32_t bs = m->block_size;
+  uint64_t h = 0;
+  int64_t i = 0;
+  for (; (i + 1) * bs <= n; ++i) {
+    h = block_hash(h, tokens + i * bs, bs);
+    if (m->lookup(h, tokens + i * bs) < 0) break;
+  }
+  return i * bs;
+}
+
+int pkv_bm_preempt(pkv_block_manager* m, int64_t* seq_id, int64_t* num_cached_tokens) {
+  std::lock_guard<std::mutex> g(m->mu);
+  if (m->seqs.empty()) return bm_fail(PKV_ERR_INVALID_ARG, "no sequence holds blocks");
+  auto victim = m->seqs.begin();
+  for (auto it = m->seqs.begin(); it != m->seqs.end(); ++it)
+    if (it->second.order > victim->second.order) victim = it;
+  m->release_all(victim->second.blocks);
+  const int64_t cached = cached_prefix(m, victim->second.tokens.data(), (int64_t)victim->second.tokens.size());
+  if (seq_id) *seq_id = victim->first;
+  if (num_cached_tokens) *num_cached_tokens = cached;
+  m->seqs.erase(victim);
   return PKV_OK;
 }
 

@@ -113,8 +113,10 @@ def test_random_operations_keep_invariants():
     bs, nb = 4, 64
     bm = pkv.BlockManager(nb, bs)
     live = {}
+    order = []  # allocation order of the live sequences
     prefixes = [list(rng.integers(0, 50, size=8)) for _ in range(3)]
     next_id = 0
+    preempted = 0
     for step in range(600):
         op = rng.random()
         if op < 0.35 or not live:
@@ -124,8 +126,20 @@ def test_random_operations_keep_invariants():
                 bm.allocate(next_id, toks)
                 assert ok
                 live[next_id] = list(toks)
+                order.append(next_id)
             except pkv.OutOfBlocks:
                 assert not ok
+                if live and rng.random() < 0.5:
+                    # scheduler response: preempt the newest sequence, then retry once
+                    victim, cached = bm.preempt()
+                    assert victim == order[-1] and 0 <= cached <= len(live[victim])
+                    order.pop()
+                    del live[victim]
+                    preempted += 1
+                    if bm.can_allocate(toks):
+                        bm.allocate(next_id, toks)
+                        live[next_id] = list(toks)
+                        order.append(next_id)
             next_id += 1
         elif op < 0.75:
             sid = list(live)[rng.integers(0, len(live))]
@@ -141,6 +155,7 @@ def test_random_operations_keep_invariants():
             sid = list(live)[rng.integers(0, len(live))]
             bm.free(sid)
             del live[sid]
+            order.remove(sid)
         # invariants: refcounts equal the number of tables holding a block; shared
         # blocks are full blocks holding the same tokens in every holder
         holders = {}
@@ -155,3 +170,69 @@ def test_random_operations_keep_invariants():
             if len(contents) > 1:
                 assert len(set(contents)) == 1 and len(contents[0]) == bs
         assert bm.num_free_blocks == nb - len(holders)
+    assert preempted > 0
+
+
+def test_exhaust_preempt_retry():
+    """Pool runs out -> the most recently allocated sequence is preempted (its
+    blocks freed, registered blocks kept in the prefix cache) -> the allocation
+    that failed succeeds; the victim re-allocated later reuses what the cache
+    still holds (page "Nano-vLLM Architecture and Performance", Key Features,
+    preemption on exhausted KV cache)."""
+    bs = 4
+    bm = pkv.BlockManager(10, bs)
+    shared = [1, 2, 3, 4, 5, 6, 7, 8]                      # two full blocks
+    p1 = shared + [9, 10]                                   # 3 blocks, 2 shared later
+    p2 = shared + [20, 21, 22]                              # shares p1's 2 full blocks
+    p3 = [30 + i for i in range(13)]                        # 4 blocks (3 full + 1 partial)
+    assert bm.allocate(1, p1) == 0
+    assert bm.allocate(2, p2) == 8
+    assert bm.allocate(3, p3) == 0
+    assert bm.num_free_blocks == 10 - 3 - 1 - 4
+    p4 = [50 + i for i in range(12)]                        # needs 3 blocks, 2 are free
+    assert not bm.can_allocate(p4)
+    with pytest.raises(pkv.OutOfBlocks):
+        bm.allocate(4, p4)
+    assert bm.num_free_blocks == 2                          # the failed call changed nothing
+    t3 = bm.block_table(3)
+    victim, cached = bm.preempt()
+    assert victim == 3                                      # the most recent allocation
+    assert cached == 12                                     # its 3 full blocks stay registered
+    assert bm.num_free_blocks == 6 and all(bm.refcount(b) == 0 for b in t3)
+    with pytest.raises(pkv.PkvError):
+        bm.seq_len(3)
+    assert bm.allocate(4, p4) == 0                          # the retry succeeds
+    # the shared prefix is untouched by the preemption
+    t1, t2 = bm.block_table(1), bm.block_table(2)
+    assert list(t1[:2]) == list(t2[:2]) and bm.refcount(t1[0]) == 2
+    # p4 took 3 of the 6 free blocks, oldest first: the 2 never-used blocks and the
+    # victim's partial block (freed first, being its last); its 3 full blocks stay cached
+    assert sorted(set(bm.block_table(4)) & set(t3)) == [t3[3]]
+    bm.free(1)                                              # returns p1's own tail block only
+    assert bm.refcount(t1[0]) == 1 and bm.num_free_blocks == 4
+    assert bm.allocate(3, p3) == 12                         # the victim comes back, 12 tokens cached
+    assert list(bm.block_table(3)[:3]) == list(t3[:3])
+    assert bm.num_free_blocks == 0
+
+
+def test_append_exhaustion_preempts_the_newest():
+    bm = pkv.BlockManager(4, 2)
+    bm.allocate(1, [1, 2])                                  # 1 full block
+    bm.allocate(2, [3, 4, 5])                               # 2 blocks
+    bm.allocate(3, [6])                                     # 1 block; pool now empty
+    assert bm.num_free_blocks == 0
+    bm.append(3, 7)                                         # fills seq 3's block: no new block
+    with pytest.raises(pkv.OutOfBlocks):
+        bm.append(1, 8)                                     # seq 1 needs a new block
+    assert bm.seq_len(1) == 2
+    victim, cached = bm.preempt()
+    assert victim == 3 and cached == 2                      # its block was completed by the append
+    slot = bm.append(1, 8)
+    assert slot // 2 in bm.block_table(1) and bm.seq_len(1) == 3
+    victim, _ = bm.preempt()
+    assert victim == 2
+    victim, _ = bm.preempt()
+    assert victim == 1
+    with pytest.raises(pkv.PkvError):
+        bm.preempt()                                        # nothing left
+    assert bm.num_free_blocks == 4
