@@ -603,6 +603,7 @@ int pkv_paged_prefill_attn(const void* q, const void* k, const void* v, const in
       a.plan_queue = p.hdr;
       a.plan_items = p.items;
       a.plan_arrive = p.arrive;
+      a.plan_mailbox = reinterpret_cast<int32_t*>(w + L.mailbox);
       a.plan_states = reinterpret_cast<float*>(w + L.states);
 #ifdef PKV_PREFILL_TIMELINE
       a.timeline = reinterpret_cast<long long*>(w + L.timeline);

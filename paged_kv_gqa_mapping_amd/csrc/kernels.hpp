@@ -95,7 +95,8 @@ struct PrefillArgs {
   const int32_t* plan_hdr;
   int32_t* plan_queue;
   const int32_t* plan_items;
-  int32_t* plan_arrive;
+  int32_t* plan_arrive;    // per split query tile and wave
+  int32_t* plan_mailbox;   // per workgroup, two words: the item index claimed for it, by item parity
   float* plan_states;
   int32_t items_cap;
   // built with PKV_PREFILL_TIMELINE only: per workgroup and item, timestamps
@@ -118,6 +119,11 @@ constexpr int kTimelineFields = 8;
 constexpr int kPlanXcds = 8;
 constexpr int kPlanCusPerXcd = 32;
 constexpr int kPersistWgs = kPlanXcds * kPlanCusPerXcd;
+// waves per workgroup of the prefill kernels (each merges its own columns of a split tile)
+constexpr int kPlanWaves = 8;
+// items a workgroup takes by its index before it claims from the die's queue
+// (the next items are known two ahead, so their copies can be issued early)
+constexpr int kPlanStaticItems = 3;
 // pieces are at least kPlanMinCap key tiles; the cap is chosen so that each
 // die's list holds about kPlanItemsPerCu maximal pieces per workgroup
 #ifndef PKV_PLAN_ITEMS_PER_CU
@@ -139,7 +145,7 @@ struct PrefillPlanLayout {
   int32_t split_cap;  // split query tiles (arrival counters)
   int32_t slot_cap;   // softmax-state slots
   int64_t state_floats;  // floats per slot
-  int64_t hdr, items, arrive, states, timeline, total;  // byte offsets, total bytes
+  int64_t hdr, items, arrive, mailbox, states, timeline, total;  // byte offsets, total bytes
 };
 
 __host__ __device__ inline int64_t plan_align(int64_t x) { return (x + 255) & ~(int64_t)255; }
@@ -160,7 +166,8 @@ __host__ __device__ inline PrefillPlanLayout prefill_plan_layout(int32_t num_seq
   int64_t off = 0;
   L.hdr = off;     off = plan_align(off + kHdrInts * 4);
   L.items = off;   off = plan_align(off + (int64_t)kPlanXcds * L.items_cap * kItemInts * 4);
-  L.arrive = off;  off = plan_align(off + (int64_t)L.split_cap * 4);
+  L.arrive = off;  off = plan_align(off + (int64_t)L.split_cap * kPlanWaves * 4);
+  L.mailbox = off; off = plan_align(off + (int64_t)kPersistWgs * 2 * 4);
   L.states = off;  off = plan_align(off + (int64_t)L.slot_cap * L.state_floats * 4);
 #ifdef PKV_PREFILL_TIMELINE
   L.timeline = off; off = plan_align(off + (int64_t)kPersistWgs * kTimelineItems * kTimelineFields * 8);

@@ -185,11 +185,11 @@ __global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillPlanA
   if (overflow) atomicOr(&s_overflow, 1);
   __syncthreads();
 
-  // 7. header: queue heads start past the first item of every workgroup (taken
-  // by workgroup index), item counts, and the arrival counters zeroed
-  const int splits = min(s_scan[kPlanXcds][kPlanThreads - 1], p.split_cap);
+  // 7. header: queue heads start past the items every workgroup takes by its
+  // index, item counts, and the arrival counters (one per split tile and wave) zeroed
+  const int splits = min(s_scan[kPlanXcds][kPlanThreads - 1], p.split_cap) * kPlanWaves;
   if (tid < kPlanXcds) {
-    p.hdr[tid] = kPlanCusPerXcd;
+    p.hdr[tid] = kPlanStaticItems * kPlanCusPerXcd;
     p.hdr[kPlanXcds + tid] = min(s_scan[tid][kPlanThreads - 1], p.items_cap);
   }
   if (tid == 0) {
