@@ -222,40 +222,47 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a
 
 // ---------------------------------------------------------------- persistent stream
 
-// The fields of an item that the stream keeps (wave-uniform): key tiles
-// [kt_lo, kt_hi) of its query tile; piece pc & 0xffff of pc >> 16 of a split
-// query tile whose arrival counters start at split * 8 and whose state slots
-// start at `slot` (split < 0: a whole query tile).
-struct Hot {
-  int kt_lo, kt_hi, split, slot, pc;
-};
+// The kernel's arguments, read from the kernel argument segment where this is
+// called.  The persistent kernel's scalar registers are too few to hold every
+// argument across its loop, so the ones used once per item are loaded again
+// at each use (the empty asm makes the pointer opaque, so that the loads are
+// neither hoisted out of the loop nor merged).
+__device__ __forceinline__ const PrefillArgs& args_here() {
+  typedef const __attribute__((address_space(4))) PrefillArgs const_args_t;
+  const_args_t* p = (const_args_t*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  return *(const PrefillArgs*)p;
+}
 
-// This wave's columns of an item: each column's position (the last key past
-// the sequence's queries) and row of q and out (times Hq, plus the head; -1
-// past the queries); the block's first position and the end of the key tiles
-// the wave computes (wave-uniform).
-struct Cols {
+// record idx of die xcd's list
+__device__ __forceinline__ const_i32_t* item_record(const PrefillArgs& a, int xcd, int idx) {
+  return (const_i32_t*)a.plan_items + ((int64_t)xcd * a.items_cap + idx) * kItemInts;
+}
+
+// The part of an item the stream keeps in scalar registers: its key tiles
+// [kt_lo, kt_hi), and for this wave the block's first position and the end of
+// the key tiles it computes; per lane, each column's position (the last key
+// past the sequence's queries) and row of q and out (times Hq, plus the head;
+// -1 past the queries).  The rest of the record (piece, split) is read again
+// when the item ends.
+struct Item2 {
+  int kt_lo, kt_hi, min_pos, n_kt_wave;
   int pos;
   int64_t q_row;
-  int min_pos, n_kt_wave;
   __device__ __forceinline__ bool valid() const { return q_row >= 0; }
 };
 
-// Item idx of die xcd's list: the fields kept, where its K/V rows are, and this
-// wave's columns.  Record fields and sequence lengths are scalar loads.
+// Item idx of die xcd's list: what the stream keeps of it, and where its K/V rows are.
 template <int D, int HW>
-__device__ __forceinline__ void load_item(const PrefillArgs& a, int xcd, int idx, int wave, int col, Hot& x,
-                                          TileSource<D>& src, Cols& cl) {
+__device__ __forceinline__ void load_item(const PrefillArgs& a, int xcd, int idx, int wave, int col, Item2& x,
+                                          TileSource<D>& src) {
   constexpr int QP = 32 * (kCB / HW);
-  const_i32_t* rec = (const_i32_t*)a.plan_items + ((int64_t)xcd * a.items_cap + idx) * kItemInts;
+  const_i32_t* rec = item_record(a, xcd, idx);
   const int b = rec[kItB];
   const int hg = rec[kItHg];
   const int tile = rec[kItTile];
   x.kt_lo = rec[kItKtLo];
   x.kt_hi = rec[kItKtHi];
-  x.pc = rec[kItChunk];
-  x.split = rec[kItSplit];
-  x.slot = rec[kItSlot];
   const_i32_t* cq = (const_i32_t*)a.cu_seqlens_q;
   const_i32_t* ck = (const_i32_t*)a.cu_seqlens_k;
   const int q0 = cq[b];
@@ -269,11 +276,11 @@ __device__ __forceinline__ void load_item(const PrefillArgs& a, int xcd, int idx
   const int qi = first + col;
   const int shift = Lk - Lq;
   const bool valid = qi < Lq;
-  cl.pos = valid ? shift + qi : Lk - 1;
-  cl.q_row = valid ? (int64_t)(q0 + qi) * Hq + head : -1;
-  cl.min_pos = shift + first;
+  x.pos = valid ? shift + qi : Lk - 1;
+  x.q_row = valid ? (int64_t)(q0 + qi) * Hq + head : -1;
+  x.min_pos = shift + first;
   const int w_max_pos = first < Lq ? shift + min(first + 32, Lq) - 1 : -1;
-  cl.n_kt_wave = w_max_pos >= 0 ? min(x.kt_hi, w_max_pos / kKT + 1) : x.kt_lo;
+  x.n_kt_wave = w_max_pos >= 0 ? min(x.kt_hi, w_max_pos / kKT + 1) : x.kt_lo;
 }
 
 // A piece of a split query tile, one wave's columns: write the state (the O^T
@@ -294,14 +301,12 @@ __device__ __forceinline__ void load_item(const PrefillArgs& a, int xcd, int idx
 // starts).  This runs before the next tile's copies are issued, so the wait
 // covers only the state stores.
 template <int D>
-__device__ __forceinline__ void finish_piece(const PrefillArgs& a, const Hot& x, const Cols& cl,
-                                             const WaveTile<D>& wt, int wave, int lane) {
+__device__ __forceinline__ void finish_piece(const PrefillArgs& a, int split, int slot, int piece, int pieces,
+                                             int64_t q_row, const WaveTile<D>& wt, int wave, int lane) {
   using Gm = Geom<D>;
   constexpr int NR = Gm::MD * 16 + 2;  // floats per lane of a wave's state
-  const int piece = x.pc & 0xffff;
-  const int pieces = x.pc >> 16;
   const int64_t slot_floats = (int64_t)kWaves * NR * 64;
-  float* const wbase = a.plan_states + (int64_t)x.slot * slot_floats + (int64_t)wave * NR * 64 + lane;
+  float* const wbase = a.plan_states + (int64_t)slot * slot_floats + (int64_t)wave * NR * 64 + lane;
   auto at = [&](int j, int r) { return wbase + j * slot_floats + r * 64; };
   const float l = halves_sum(wt.lsum);
 #pragma unroll
@@ -313,8 +318,7 @@ __device__ __forceinline__ void finish_piece(const PrefillArgs& a, const Hot& x,
   wait_vmem<0>();
   int old = 0;
   if (lane == 0)
-    old = __hip_atomic_fetch_add(a.plan_arrive + x.split * kWaves + wave, 1, __ATOMIC_RELAXED,
-                                 __HIP_MEMORY_SCOPE_AGENT);
+    old = __hip_atomic_fetch_add(a.plan_arrive + split * kWaves + wave, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   asm volatile("" ::: "memory");  // the other pieces' states are read after the count
   if (uniform(old) != pieces - 1) return;
   // M = max_j m_j; L = sum_j 2^(m_j - M) l_j; out = sum_j 2^(m_j - M) o_j / L, in piece order
@@ -326,10 +330,10 @@ __device__ __forceinline__ void finish_piece(const PrefillArgs& a, const Hot& x,
     const float lj = j == piece ? l : *at(j, Gm::MD * 16 + 1);
     L = fmaf(exp2_hw(mj - M), lj, L);
   }
-  if (!cl.valid()) return;
+  if (q_row < 0) return;
   const float inv = 1.0f / L;
   const int half = lane >> 5;
-  uint16_t* op = (uint16_t*)a.out + cl.q_row * D + half * 4;
+  uint16_t* op = (uint16_t*)a.out + q_row * D + half * 4;
 #pragma unroll
   for (int md = 0; md < Gm::MD; ++md) {
     float o[16];
@@ -356,26 +360,30 @@ __device__ __forceinline__ void finish_piece(const PrefillArgs& a, const Hot& x,
   }
 }
 
-// the end of an item for one wave: its output, or its state as a piece
+// The end of item idx for one wave: its output (if the wave computed any of
+// its key tiles), or its state as a piece.
 template <int D>
-__device__ __forceinline__ void finish_item(const PrefillArgs& a, const Hot& x, const Cols& cl,
+__device__ __forceinline__ void finish_item(const PrefillArgs& a, int xcd, int idx, int64_t q_row, bool computed,
                                             const WaveTile<D>& wt, const Lanes<D>& ln) {
-  if (x.split < 0) {
-    if (cl.n_kt_wave > x.kt_lo) wt.store_out(a.out, cl.q_row, ln.half, cl.valid());
+  const_i32_t* rec = item_record(a, xcd, idx);
+  const int split = rec[kItSplit];
+  if (split < 0) {
+    if (computed) wt.store_out(a.out, q_row, ln.half, q_row >= 0);
   } else {
-    finish_piece<D>(a, x, cl, wt, ln.wave, ln.lane);
+    const int pc = rec[kItChunk];
+    finish_piece<D>(a, split, rec[kItSlot], pc & 0xffff, pc >> 16, q_row, wt, ln.wave, ln.lane);
   }
 }
 
 // timeline stamps (a diagnostic; compiled in with PKV_PREFILL_TIMELINE only):
 // per workgroup and item, fields 0 workgroup | die << 32, 1 kt_lo | kt_hi << 32,
-// 2 split + 1, 4 start, 5 the previous item finished, 6 this item's tiles done
-__device__ __forceinline__ void stamp(const PrefillArgs& a, int n, int field, long long v) {
+// 2 item index, 4 start, 5 the previous item finished, 6 this item's tiles done
+__device__ __forceinline__ void stamp(int n, int field, long long v) {
 #ifdef PKV_PREFILL_TIMELINE
+  const PrefillArgs& a = args_here();
   if (a.timeline && n < kTimelineItems && threadIdx.x == 0)
     a.timeline[((int64_t)blockIdx.x * kTimelineItems + n) * kTimelineFields + field] = v;
 #else
-  (void)a;
   (void)n;
   (void)field;
   (void)v;
@@ -387,18 +395,6 @@ __device__ __forceinline__ long long stamp_now() {
 #else
   return 0;
 #endif
-}
-
-// The kernel's arguments, read from the kernel argument segment where this is
-// called.  The persistent kernel's scalar registers are too few to hold every
-// argument across its loop, so the ones used once per item are loaded again
-// at each use (the empty asm makes the pointer opaque, so that the loads are
-// neither hoisted out of the loop nor merged).
-__device__ __forceinline__ const PrefillArgs& args_here() {
-  typedef const __attribute__((address_space(4))) PrefillArgs const_args_t;
-  const_args_t* p = (const_args_t*)__builtin_amdgcn_kernarg_segment_ptr();
-  asm volatile("" : "+s"(p));
-  return *(const PrefillArgs*)p;
 }
 
 template <int D, int HW>
@@ -421,16 +417,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_stream_kernel(PrefillArgs
     constexpr bool is_late = decltype(LATE)::value;
     // the items known ahead: cur (being computed), nxt and the index of the one
     // after it (an index >= count: none)
+    int idx_cur = wgi;
     int idx_nxt = wgi + kPlanCusPerXcd;
     int idx_nn = wgi + 2 * kPlanCusPerXcd;
-    Hot cur, nxt;
+    Item2 cur, nxt;
     TileSource<D> src_cur, src_nxt;
-    Cols cl, ncl;
-    load_item<D, HW>(args_here(), xcd, wgi, ln.wave, ln.col, cur, src_cur, cl);
+    load_item<D, HW>(args_here(), xcd, idx_cur, ln.wave, ln.col, cur, src_cur);
     nxt = cur;
     src_nxt = src_cur;
-    ncl = cl;
-    if (idx_nxt < count) load_item<D, HW>(args_here(), xcd, idx_nxt, ln.wave, ln.col, nxt, src_nxt, ncl);
+    if (idx_nxt < count) load_item<D, HW>(args_here(), xcd, idx_nxt, ln.wave, ln.col, nxt, src_nxt);
     int claimed = 0;  // lane 0 of wave 0: the item claimed for the one after idx_nn
     if (idx_nn < count && threadIdx.x == 0)
       claimed = __hip_atomic_fetch_add(args_here().plan_queue + xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -457,18 +452,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_stream_kernel(PrefillArgs
 
     WaveTile<D> wt;
     wt.reset();
-    wt.load_q(args_here().q, cl.q_row, cl.valid(), ln.half);
+    wt.load_q(args_here().q, cur.q_row, cur.valid(), ln.half);
     wt.settle_q();
 
     int gt = 0;  // stream tile counter: K buffer gt & 1
     int vprev = kVBufs - 1, vcur = 0, vnext = 1 % kVBufs;
-    Hot prv = cur;
-    Cols pcl = cl;
+    // the previous item, finished at the top of the next item's first tile
+    int idx_prv = idx_cur;
+    int64_t q_row_prv = cur.q_row;
+    bool computed_prv = false, late_pv_prv = false;
     int n_item = 0;
-    stamp(args_here(), n_item, 0, (long long)wgi | ((long long)xcd << 32));
-    stamp(args_here(), n_item, 1, (long long)cur.kt_lo | ((long long)cur.kt_hi << 32));
-    stamp(args_here(), n_item, 2, (long long)(cur.split + 1));
-    stamp(args_here(), n_item, 4, stamp_now());
+    stamp(n_item, 0, (long long)wgi | ((long long)xcd << 32));
+    stamp(n_item, 1, (long long)cur.kt_lo | ((long long)cur.kt_hi << 32));
+    stamp(n_item, 2, idx_cur);
+    stamp(n_item, 4, stamp_now());
     int kt = cur.kt_lo;
     for (;;) {
       wait_vmem<0>();
@@ -476,11 +473,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_stream_kernel(PrefillArgs
       if (kt == cur.kt_lo && n_item > 0) {
         // the previous item's end: a late wave's last P V product, then its output or state
         if constexpr (is_late)
-          if (pcl.n_kt_wave == prv.kt_hi && prv.kt_hi > prv.kt_lo) wt.template pv<false>(lds, ln, vprev);
-        finish_item<D>(args_here(), prv, pcl, wt, ln);
+          if (late_pv_prv) wt.template pv<false>(lds, ln, vprev);
+        finish_item<D>(args_here(), xcd, idx_prv, q_row_prv, computed_prv, wt, ln);
         wt.reset();
         wt.settle_q();  // cur's queries (loaded during the previous item's last tile) are in
-        stamp(args_here(), n_item, 5, stamp_now());
+        stamp(n_item, 5, stamp_now());
       }
       // copies of the tile after this one in the stream
       if (csel < 2) {
@@ -500,18 +497,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_stream_kernel(PrefillArgs
       const bool last = kt + 1 >= cur.kt_hi;
       // compute tile kt of cur
       if constexpr (is_late) {
-        if (kt > cur.kt_lo && kt <= cl.n_kt_wave) wt.template pv<false>(lds, ln, vprev);
-        if (kt < cl.n_kt_wave) wt.template qk_softmax<false>(lds, ln, gt & 1, kt * kKT, 0, cl.pos, cl.min_pos, c);
+        if (kt > cur.kt_lo && kt <= cur.n_kt_wave) wt.template pv<false>(lds, ln, vprev);
+        if (kt < cur.n_kt_wave) wt.template qk_softmax<false>(lds, ln, gt & 1, kt * kKT, 0, cur.pos, cur.min_pos, c);
       } else {
-        if (kt < cl.n_kt_wave) {
-          wt.template qk_softmax<true>(lds, ln, gt & 1, kt * kKT, vcur, cl.pos, cl.min_pos, c);
+        if (kt < cur.n_kt_wave) {
+          wt.template qk_softmax<true>(lds, ln, gt & 1, kt * kKT, vcur, cur.pos, cur.min_pos, c);
           if (!last) wt.template pv<true>(lds, ln, vcur);
         }
       }
       // the next item's queries, once this wave's last Q K^T of cur is done
-      if (last && idx_nxt < count) wt.load_q(args_here().q, ncl.q_row, ncl.valid(), ln.half);
+      if (last && idx_nxt < count) wt.load_q(args_here().q, nxt.q_row, nxt.valid(), ln.half);
       if constexpr (!is_late)
-        if (last && kt < cl.n_kt_wave) wt.template pv<true>(lds, ln, vcur);
+        if (last && kt < cur.n_kt_wave) wt.template pv<true>(lds, ln, vcur);
       // block ids of the copy cursor's tile (they arrive while this wave waits at the next barrier)
       prefetch_blocks();
       if (kt == cur.kt_lo && idx_nxt < count && n_item > 0) {
@@ -537,16 +534,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_stream_kernel(PrefillArgs
       }
       // cur's tiles are done: wave 0 publishes the item it claimed when cur began
       if (threadIdx.x == 0 && idx_nn < count) args_here().plan_mailbox[2 * blockIdx.x + (n_item & 1)] = claimed;
-      stamp(args_here(), n_item, 6, stamp_now());
+      stamp(n_item, 6, stamp_now());
       if (idx_nxt >= count) break;
-      prv = cur;
-      pcl = cl;
+      idx_prv = idx_cur;
+      q_row_prv = cur.q_row;
+      computed_prv = cur.n_kt_wave > cur.kt_lo;
+      late_pv_prv = cur.n_kt_wave == cur.kt_hi && cur.kt_hi > cur.kt_lo;
+      idx_cur = idx_nxt;
       cur = nxt;
-      cl = ncl;
       src_cur = src_nxt;
       idx_nxt = idx_nn;
       idx_nn = count;  // learned at the end of the new item's first tile
-      if (idx_nxt < count) load_item<D, HW>(args_here(), xcd, idx_nxt, ln.wave, ln.col, nxt, src_nxt, ncl);
+      if (idx_nxt < count) load_item<D, HW>(args_here(), xcd, idx_nxt, ln.wave, ln.col, nxt, src_nxt);
       // the copy cursor was in the old nxt (now cur) or past it
       if (csel == 1) {
         csel = 0;
@@ -558,17 +557,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_stream_kernel(PrefillArgs
       if (idx_nxt < count && threadIdx.x == 0)
         claimed = __hip_atomic_fetch_add(args_here().plan_queue + xcd, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       ++n_item;
-      stamp(args_here(), n_item, 0, (long long)wgi | ((long long)xcd << 32));
-      stamp(args_here(), n_item, 1, (long long)cur.kt_lo | ((long long)cur.kt_hi << 32));
-      stamp(args_here(), n_item, 2, (long long)(cur.split + 1));
-      stamp(args_here(), n_item, 4, stamp_now());
+      stamp(n_item, 0, (long long)wgi | ((long long)xcd << 32));
+      stamp(n_item, 1, (long long)cur.kt_lo | ((long long)cur.kt_hi << 32));
+      stamp(n_item, 2, idx_cur);
+      stamp(n_item, 4, stamp_now());
       kt = cur.kt_lo;
     }
     // the last item's end (no copies are in flight any more)
     if constexpr (is_late)
-      if (cl.n_kt_wave == cur.kt_hi && cur.kt_hi > cur.kt_lo) wt.template pv<false>(lds, ln, vprev);
-    finish_item<D>(args_here(), cur, cl, wt, ln);
-    stamp(args_here(), n_item + 1, 0, -1);
+      if (cur.n_kt_wave == cur.kt_hi && cur.kt_hi > cur.kt_lo) wt.template pv<false>(lds, ln, vprev);
+    finish_item<D>(args_here(), xcd, idx_cur, cur.q_row, cur.n_kt_wave > cur.kt_lo, wt, ln);
+    stamp(n_item + 1, 0, -1);
   };
   if (kSkew && ln.wave >= kWaves / 2)
     stream(std::true_type{});

@@ -181,6 +181,30 @@ struct Lanes {
   }
 };
 
+// One wave's copies of one tile: where every row the wave copies exists
+// (`whole`), the byte offsets (in the pool, head included) of its groups of 8
+// rows, each group in one block, and issue(i) issues copy instruction i (K for
+// i < IPW, then V) from them with two scalar additions; otherwise the copies
+// were issued when the tile was planned and issue(i) does nothing.
+template <int D>
+struct TileCopy {
+  using Gm = Geom<D>;
+  int64_t off[Gm::NBLK];
+  bool whole;
+
+  __device__ __forceinline__ void issue(const PrefillArgs& a, uint8_t* lds, const Lanes<D>& ln, int kb, int vb,
+                                        int i) const {
+    if (!whole) return;
+    const int ii = i % Gm::IPW;
+    const bool is_v = i >= Gm::IPW;
+    const uint32_t dst = uniform(lds_addr(&lds[(is_v ? kKBufs + vb : kb) * Gm::TILEB]) +
+                                 Gm::RW * ln.wave * Gm::ROWB + ii * 1024);
+    const uint8_t* bytes = (const uint8_t*)(is_v ? a.v : a.k);
+    const int64_t row_bytes = (int64_t)a.num_kv_heads * Gm::ROWB;
+    copy_to_lds(bytes + off[(ii * Gm::RPI) / 8] + ((ii * Gm::RPI) % 8) * row_bytes, ln.src[i], dst);
+  }
+};
+
 // Where one item's K/V rows are: through a block table row (paged) or packed
 // rows from k0, for the keys [key_base, key_base + last_key + 1) of the
 // sequence, of KV head g (all wave-uniform).  Tile t of the item holds its
@@ -221,36 +245,48 @@ struct TileSource {
   // computes its own row.
   __device__ __forceinline__ void issue(const PrefillArgs& a, uint8_t* lds, const Lanes<D>& ln,
                                         const int32_t (&blk)[Gm::NBLK], int t, int kb, int vb) const {
+    const TileCopy<D> tc = plan(a, lds, ln, blk, t, kb, vb);
+#pragma unroll
+    for (int i = 0; i < 2 * Gm::IPW; ++i) tc.issue(a, lds, ln, kb, vb, i);
+  }
+
+  // The copies of tile t for one wave.  Where every row the wave copies exists,
+  // they are left to TileCopy::issue; a tile that reaches past the last key is
+  // copied here, with per-lane row addresses.
+  __device__ __forceinline__ TileCopy<D> plan(const PrefillArgs& a, uint8_t* lds, const Lanes<D>& ln,
+                                              const int32_t (&blk)[Gm::NBLK], int t, int kb, int vb) const {
+    TileCopy<D> tc;
     const int lbs = a.log2_block_size;
     const int bs_mask = (1 << lbs) - 1;
     const int64_t row_bytes = (int64_t)a.num_kv_heads * Gm::ROWB;
-    const int64_t blk_bytes = row_bytes << lbs;
-    const bool whole = t * kKT + Gm::RW * ln.wave + Gm::RW - 1 <= last_key;  // every row this wave copies exists
+    tc.whole = t * kKT + Gm::RW * ln.wave + Gm::RW - 1 <= last_key;  // every row this wave copies exists
+    // rows RW w + 8 j .. + 7 of the tile: one block, consecutive rows in it
+#pragma unroll
+    for (int j = 0; j < Gm::NBLK; ++j) {
+      const int rj = t * kKT + Gm::RW * ln.wave + 8 * j;
+      const int64_t row = table ? ((int64_t)blk[j] << lbs) + ((key_base + rj) & bs_mask) : (int64_t)(k0 + rj);
+      tc.off[j] = row * row_bytes + head_bytes;
+    }
+    if (tc.whole) return tc;
     const int lr = ln.lane / Gm::CPR;
     const int ls = ln.lane % Gm::CPR;
+    const int64_t blk_bytes = row_bytes << lbs;
 #pragma unroll
     for (int i = 0; i < 2 * Gm::IPW; ++i) {
       const int ii = i % Gm::IPW;
       const bool is_v = i >= Gm::IPW;
-      const int bi = is_v ? kKBufs + vb : kb;
-      const uint32_t dst = uniform(lds_addr(&lds[bi * Gm::TILEB]) + Gm::RW * ln.wave * Gm::ROWB + ii * 1024);
+      const uint32_t dst = uniform(lds_addr(&lds[(is_v ? kKBufs + vb : kb) * Gm::TILEB]) +
+                                   Gm::RW * ln.wave * Gm::ROWB + ii * 1024);
       const uint8_t* bytes = (const uint8_t*)(is_v ? a.v : a.k);
-      if (whole) {
-        const int r0 = t * kKT + Gm::RW * ln.wave + ii * Gm::RPI;  // first row of the instruction
-        const int64_t row0 = table ? (int64_t)blk[(ii * Gm::RPI) / 8] * blk_bytes +
-                                         (int64_t)((key_base + r0) & bs_mask) * row_bytes
-                                   : (int64_t)(k0 + r0) * row_bytes;
-        copy_to_lds(bytes + row0 + head_bytes, ln.src[i], dst);
-      } else {
-        const int rt = Gm::RW * ln.wave + ii * Gm::RPI + lr;  // row within the tile
-        const int tc = min(t * kKT + rt, last_key);
-        const int64_t row = table ? (int64_t)blk[(ii * Gm::RPI) / 8] * blk_bytes +
-                                        (int64_t)((key_base + tc) & bs_mask) * row_bytes
-                                  : (int64_t)(k0 + tc) * row_bytes;
-        const int ch = is_v ? (ls - vrot<D>(rt)) & (Gm::CPR - 1) : (ls - rt) & (Gm::CPR - 1);
-        copy_to_lds(bytes + row + head_bytes + 16 * ch, dst);
-      }
+      const int rt = Gm::RW * ln.wave + ii * Gm::RPI + lr;  // row within the tile
+      const int tcl = min(t * kKT + rt, last_key);
+      const int64_t row = table ? (int64_t)blk[(ii * Gm::RPI) / 8] * blk_bytes +
+                                      (int64_t)((key_base + tcl) & bs_mask) * row_bytes
+                                : (int64_t)(k0 + tcl) * row_bytes;
+      const int ch = is_v ? (ls - vrot<D>(rt)) & (Gm::CPR - 1) : (ls - rt) & (Gm::CPR - 1);
+      copy_to_lds(bytes + row + head_bytes + 16 * ch, dst);
     }
+    return tc;
   }
 };
 
