@@ -138,12 +138,20 @@ int pkv_rope_kv_store(void* q, const void* k, const void* v, const int32_t* posi
  * workspace, and a reduction pass merges the splits of each (sequence, head).
  * A sequence that fits one split has its output written by the first pass.
  *
- * pkv_decode_split_tokens returns the split length the library picks for a
- * shape (a multiple of 64); pass it, or 0 for the same choice, or any
- * positive multiple of 64.
- * pkv_decode_workspace_bytes gives the workspace size that split length
- * needs (0 when no sequence can span two splits).
+ * split_tokens = PKV_SPLIT_BALANCED instead cuts the batch's total context
+ * into about 1024 pieces of equal length (at most T tokens, T a multiple of
+ * 64 chosen on the device from context_lens; every sequence gets at least
+ * one piece), so that the waves of the first pass carry equal work however
+ * the context lengths are mixed.
+ *
+ * pkv_decode_split_tokens returns the split the library picks for a shape (a
+ * multiple of 64, or PKV_SPLIT_BALANCED); pass it, or 0 for the same choice,
+ * or any positive multiple of 64, or PKV_SPLIT_BALANCED.
+ * pkv_decode_workspace_bytes gives the workspace size that split needs (0
+ * when no sequence can span two splits).
  */
+#define PKV_SPLIT_BALANCED (-1)
+
 int32_t pkv_decode_split_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                 int32_t max_context_len, int32_t block_size, int32_t dtype);
 
@@ -159,7 +167,7 @@ int64_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_
  *   max_context_len host int, at most max_blocks_per_seq * block_size
  *   scale           softmax scale (usually 1 / sqrt(head_dim))
  *   out             [num_seqs, num_q_heads, head_dim], written; must not alias an input
- *   split_tokens    0 or a positive multiple of 64
+ *   split_tokens    0, PKV_SPLIT_BALANCED or a positive multiple of 64
  *   workspace       device scratch of at least
  *                   pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
  *                   max_context_len, split) bytes (may be NULL when that is 0);

@@ -62,6 +62,8 @@ library_path = os.path.join(_HERE, "libpkv.so")
 
 PKV_F32 = 0
 PKV_BF16 = 1
+# split_tokens value for token-balanced decode pieces (PKV_SPLIT_BALANCED)
+SPLIT_BALANCED = -1
 
 _lib = None
 

@@ -85,6 +85,29 @@ int32_t auto_split(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_l
   return split;
 }
 
+// Token-balanced decode (split_tokens = PKV_SPLIT_BALANCED): the batch's
+// context is cut into about kBalancePieces pieces of equal length (at least
+// one per sequence), one wave each per group of KV heads, so that the waves
+// of a launch carry equal work whatever the mix of context lengths.
+#ifndef PKV_BALANCE_PIECES
+#define PKV_BALANCE_PIECES 1024
+#endif
+constexpr int32_t kBalancePieces = PKV_BALANCE_PIECES;
+int32_t balance_pieces(int32_t num_seqs) { return std::max(num_seqs, kBalancePieces); }
+// states [W, Hq, D] and [W, Hq, 2] floats, then [B, 2] ints of piece bounds
+int64_t balanced_state_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
+  return (int64_t)balance_pieces(num_seqs) * num_q_heads * (head_dim + 2) * (int64_t)sizeof(float) +
+         (int64_t)num_seqs * 2 * (int64_t)sizeof(int32_t);
+}
+// the library's choice for split_tokens = 0
+bool auto_balanced(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
+  (void)num_seqs;
+  (void)num_kv_heads;
+  (void)max_context_len;
+  return false;
+}
+
 struct DecodeCall {
   pkv::RowAttnArgs args;
   int32_t dtype;
@@ -169,19 +192,25 @@ int prepare_decode(DecodeCall& call, const void* q, const void* k_cache, const v
     return fail(PKV_ERR_INVALID_ARG, "max_context_len %d outside [0, max_blocks_per_seq * block_size = %lld]",
                 max_context_len, (long long)max_blocks_per_seq * block_size);
   if (!std::isfinite(scale)) return fail(PKV_ERR_INVALID_ARG, "scale is not finite");
-  if (split_tokens < 0 || split_tokens % 64)
-    return fail(PKV_ERR_INVALID_ARG, "split_tokens %d is not 0 or a positive multiple of 64", split_tokens);
-  const int32_t split =
-      plan ? plan->split : split_tokens ? split_tokens : auto_split(num_seqs, num_kv_heads, max_context_len);
-  const int32_t S = plan ? plan->S : std::max(1, (max_context_len + split - 1) / split);
+  if (split_tokens != PKV_SPLIT_BALANCED && (split_tokens < 0 || split_tokens % 64))
+    return fail(PKV_ERR_INVALID_ARG, "split_tokens %d is not 0, PKV_SPLIT_BALANCED or a positive multiple of 64",
+                split_tokens);
+  const bool balanced = !plan && (split_tokens == PKV_SPLIT_BALANCED ||
+                                  (split_tokens == 0 && auto_balanced(num_seqs, num_kv_heads, max_context_len)));
+  const int32_t split = balanced ? 0
+                        : plan   ? plan->split
+                        : split_tokens ? split_tokens
+                                       : auto_split(num_seqs, num_kv_heads, max_context_len);
+  const int32_t S = balanced ? balance_pieces(num_seqs) : plan ? plan->S : std::max(1, (max_context_len + split - 1) / split);
   const int32_t prefix_states = plan ? plan->C : 0;
-  const int64_t need = state_bytes(num_seqs, num_q_heads, head_dim, S, prefix_states);
+  const int64_t need = balanced ? balanced_state_bytes(num_seqs, num_q_heads, head_dim)
+                                : state_bytes(num_seqs, num_q_heads, head_dim, S, prefix_states);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PKV_ERR_WORKSPACE, "decode workspace of %lld bytes needed, %lld given%s", (long long)need,
                 (long long)workspace_bytes, workspace ? "" : " (NULL)");
   if (need > 0 && (reinterpret_cast<uintptr_t>(workspace) & 15u))
     return fail(PKV_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  if ((int64_t)num_seqs * (num_kv_heads) * S > 0x7fffffffLL)
+  if ((int64_t)(balanced ? 1 : num_seqs) * (num_kv_heads) * S > 0x7fffffffLL)
     return fail(PKV_ERR_UNSUPPORTED, "grid too large: reduce num_seqs or raise split_tokens");
 
   pkv::RowAttnArgs& a = call.args;
@@ -193,7 +222,12 @@ int prepare_decode(DecodeCall& call, const void* q, const void* k_cache, const v
   a.context_lens = context_lens;
   a.out = out;
   a.ws_o = need > 0 ? static_cast<float*>(workspace) : nullptr;
-  a.ws_ml = need > 0 ? a.ws_o + (int64_t)num_seqs * num_q_heads * (S + prefix_states) * head_dim : nullptr;
+  const int64_t state_rows = balanced ? (int64_t)S * num_q_heads : (int64_t)num_seqs * num_q_heads * (S + prefix_states);
+  a.ws_ml = need > 0 ? a.ws_o + state_rows * head_dim : nullptr;
+  if (balanced) {
+    a.balance_pieces = S;
+    a.piece_meta = reinterpret_cast<int32_t*>(a.ws_ml + state_rows * 2);
+  }
   a.scale_log2 = scale * 1.4426950408889634f;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
@@ -202,7 +236,7 @@ int prepare_decode(DecodeCall& call, const void* q, const void* k_cache, const v
   a.log2_block_size = log2_exact(block_size);
   a.split_tokens = split;
   a.num_splits = S;
-  a.ws_stride = S + prefix_states;
+  a.ws_stride = balanced ? 1 : S + prefix_states;
   a.prefix_chunk = plan ? plan->chunk : 0;
   call.dtype = dtype;
   call.head_dim = head_dim;
@@ -290,11 +324,13 @@ int32_t pkv_decode_split_tokens(int32_t num_seqs, int32_t num_q_heads, int32_t n
   (void)head_dim;
   (void)block_size;
   (void)dtype;
+  if (auto_balanced(num_seqs, num_kv_heads, max_context_len)) return PKV_SPLIT_BALANCED;
   return auto_split(std::max(num_seqs, 1), std::max(num_kv_heads, 1), std::max(max_context_len, 0));
 }
 
 int64_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
                                    int32_t split_tokens) {
+  if (split_tokens == PKV_SPLIT_BALANCED) return balanced_state_bytes(num_seqs, num_q_heads, head_dim);
   if (max_context_len <= 0 || split_tokens <= 0) return 0;
   const int64_t S = (max_context_len + (int64_t)split_tokens - 1) / split_tokens;
   return state_bytes(num_seqs, num_q_heads, head_dim, S, 0);
@@ -413,12 +449,14 @@ int pkv_paged_decode_attn_noalloc(const void* q, const void* k_cache, const void
                       ws, kScratchBytes);
   if (st == PKV_ERR_WORKSPACE) {
     // (the sizes were valid: the workspace is checked after them)
-    const int32_t split = split_tokens ? split_tokens : auto_split(num_seqs, num_kv_heads, max_context_len);
-    const int64_t S = (max_context_len + (int64_t)split - 1) / split;
+    const int32_t split = split_tokens ? split_tokens
+                                       : pkv_decode_split_tokens(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                                 max_context_len, block_size, dtype);
     return fail(PKV_ERR_WORKSPACE,
                 "the split states of this call need %lld bytes, above the %lld-byte scratch of the allocation-free "
                 "entry point: raise split_tokens or use pkv_paged_decode_attn with a workspace",
-                (long long)state_bytes(num_seqs, num_q_heads, head_dim, S, 0), (long long)kScratchBytes);
+                (long long)pkv_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len, split),
+                (long long)kScratchBytes);
   }
   if (st || call.empty) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -72,6 +72,15 @@ constexpr int kVBufs = kSkew ? 3 : 2;  // V tile buffers in LDS
 constexpr int kXcds = 8;  // accelerator dies (XCDs), each with its own L2
 constexpr int kWaves = kCB;
 constexpr int kThreads = 64 * kWaves;
+// Waves that copy the K/V tiles (the first kCopiers; the others only read
+// them).  With 4, the copies are issued by the early waves, which would
+// otherwise wait at the next barrier for the late ones, while the late waves
+// start their products at once.
+#ifndef PKV_PREFILL_COPIERS
+#define PKV_PREFILL_COPIERS 8
+#endif
+constexpr int kCopiers = PKV_PREFILL_COPIERS;
+static_assert(kCopiers == 8 || kCopiers == 4, "copier waves: all or the early half");
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
@@ -118,7 +127,7 @@ struct Geom {
   static constexpr int CPR = D / 8;                   // 16-byte slots per row
   static constexpr int TILEB = kKT * ROWB;            // bytes per K (or V) tile
   static constexpr int RPI = 1024 / ROWB;             // rows per copy instruction (4 or 8)
-  static constexpr int RW = kKT / kWaves;             // rows of each tile copied by one wave
+  static constexpr int RW = kKT / kCopiers;           // rows of each tile copied by one copier wave
   static constexpr int IPW = RW / RPI;                // copy instructions per wave, tile and tensor
   static constexpr int NBLK = RW / 8;                 // block ids per wave and tile (groups of 8 rows)
   static constexpr int KR = kKB * KSTEPS;             // K fragment reads per tile
@@ -194,7 +203,7 @@ struct TileCopy {
 
   __device__ __forceinline__ void issue(const PrefillArgs& a, uint8_t* lds, const Lanes<D>& ln, int kb, int vb,
                                         int i) const {
-    if (!whole) return;
+    if (!whole || ln.wave >= kCopiers) return;
     const int ii = i % Gm::IPW;
     const bool is_v = i >= Gm::IPW;
     const uint32_t dst = uniform(lds_addr(&lds[(is_v ? kKBufs + vb : kb) * Gm::TILEB]) +
@@ -230,7 +239,7 @@ struct TileSource {
   // one block (block_size >= 8), one id per group j of 8 rows (the same block for
   // both groups of 16 rows unless block_size is 8)
   __device__ __forceinline__ void fetch(int32_t (&blk)[Gm::NBLK], int t, int wave, int lbs) const {
-    if (!table) return;
+    if (!table || wave >= kCopiers) return;
 #pragma unroll
     for (int j = 0; j < Gm::NBLK; ++j)
       blk[j] = table[uniform((key_base + min(t * kKT + Gm::RW * wave + 8 * j, last_key)) >> lbs)];
@@ -260,6 +269,7 @@ struct TileSource {
     const int bs_mask = (1 << lbs) - 1;
     const int64_t row_bytes = (int64_t)a.num_kv_heads * Gm::ROWB;
     tc.whole = t * kKT + Gm::RW * ln.wave + Gm::RW - 1 <= last_key;  // every row this wave copies exists
+    if (ln.wave >= kCopiers) return tc;
     // rows RW w + 8 j .. + 7 of the tile: one block, consecutive rows in it
 #pragma unroll
     for (int j = 0; j < Gm::NBLK; ++j) {

@@ -53,7 +53,8 @@ hipError_t launch_one(const RowAttnArgs& a, hipStream_t stream) {
   constexpr int R = PKV_ROW_R ? PKV_ROW_R : ((BF16 && G == 4 && !PREFILL) ? 3 : 2);
   const int n_hg = a.num_kv_heads / HPW;
   const int64_t rows = PREFILL ? (int64_t)a.max_rows : (int64_t)a.num_splits;
-  const int64_t blocks = (int64_t)n_hg * a.num_seqs * rows;
+  const int64_t blocks =
+      (!PREFILL && a.balance_pieces > 0) ? (int64_t)n_hg * a.balance_pieces : (int64_t)n_hg * a.num_seqs * rows;
   if (blocks <= 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   if (!PREFILL && a.k_new)

@@ -89,6 +89,58 @@ __device__ __forceinline__ void store_words(char* p, const uint32_t* w) {
   *reinterpret_cast<T*>(p) = x;
 }
 
+// Wave-wide sum and inclusive prefix sum (64 lanes).
+__device__ __forceinline__ long long wave_sum_i64(long long x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Token-balanced decode: the piece a wave works on (see RowAttnArgs).  Every
+// wave derives the same piece boundaries from context_lens: the total (one
+// pass over the lengths), then each sequence's piece count and a running
+// prefix sum until the sequence holding piece w.  Returns false past the
+// last piece.
+__device__ __forceinline__ bool balanced_piece(const RowAttnArgs& a, int w, int lane, int& b, int& j, int& off_b,
+                                               int& n_b, int& len_b) {
+  const int B = a.num_seqs;
+  long long tot = 0;
+  for (int i = lane; i < B; i += 64) tot += max(a.context_lens[i], 0);
+  tot = wave_sum_i64(tot);
+  const long long room = max((long long)a.balance_pieces - B, 1LL);
+  const long long per = (tot + room - 1) / room;
+  const int T = (int)min(max(64LL, (per + 63) / 64 * 64), (long long)0x40000000);
+  int base = 0;
+  for (int i0 = 0; i0 < B; i0 += 64) {
+    const int i = i0 + lane;
+    const int L = i < B ? max(a.context_lens[i], 0) : 0;
+    const int n = i < B ? max(1, (L + T - 1) / T) : 0;
+    const int incl = wave_inclusive_scan(n, lane);
+    const int off = base + incl - n;
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(i < B && off <= w && w < off + n);
+    if (hit) {
+      const int src = __builtin_ctzll(hit);
+      b = i0 + src;
+      off_b = __builtin_amdgcn_readlane(off, src);
+      n_b = __builtin_amdgcn_readlane(n, src);
+      const int Lb = __builtin_amdgcn_readlane(L, src);
+      len_b = ((Lb + n_b - 1) / n_b + 63) / 64 * 64;
+      j = w - off_b;
+      return true;
+    }
+    base += __builtin_amdgcn_readlane(incl, 63);
+  }
+  return false;
+}
+
 // STORE: decode with the newest token's cache write fused in (k_new / v_new).
 template <bool BF16, int D, int HPW, int G, int U, int R, bool PREFILL, bool STORE>
 __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
@@ -111,8 +163,15 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
   int item = blockIdx.x;
   const int hg = item % n_hg;
   item /= n_hg;
-  const int b = item % a.num_seqs;
-  const int j_or_row = item / a.num_seqs;
+  // decode pieces: split j_or_row of sequence b, fixed length or token-balanced
+  const bool balanced = !PREFILL && a.balance_pieces > 0;
+  int b, j_or_row, off_b = 0, n_bal = 1, len_b = 0;
+  if (balanced) {
+    if (!balanced_piece(a, item, lane, b, j_or_row, off_b, n_bal, len_b)) return;
+  } else {
+    b = item % a.num_seqs;
+    j_or_row = item / a.num_seqs;
+  }
   const int g = hg * HPW + hl;
   const int Hq = a.num_q_heads;
   const int Hkv = a.num_kv_heads;
@@ -139,7 +198,8 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
     const int start = a.kv_start ? a.kv_start[b] : 0;
     split = j_or_row;
     q_row = b;
-    t0 = start + split * a.split_tokens;
+    const int piece = balanced ? len_b : a.split_tokens;
+    t0 = start + split * piece;
     if (L == 0) {
       if (split == 0) {  // an empty context gives zeros
         for (int gq = 0; gq < G; ++gq) {
@@ -151,7 +211,7 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
       return;
     }
     if (t0 >= L) return;
-    t1 = min(L, t0 + a.split_tokens);
+    t1 = min(L, t0 + piece);
     if (STORE && t1 == L) {
       // the step holding the newest token is taken out of the streaming loop
       // and done after it, with that token read from k_new / v_new
@@ -160,7 +220,11 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
       t1 = t_fin;
     }
     // states merged for this row: its splits, plus the group pass's when it has a prefix
-    nsplit_b = (L - start + a.split_tokens - 1) / a.split_tokens + (start > 0 ? 1 : 0);
+    nsplit_b = balanced ? n_bal : (L - start + a.split_tokens - 1) / a.split_tokens + (start > 0 ? 1 : 0);
+    if (balanced && split == 0 && hg == 0 && lane == 0) {
+      a.piece_meta[2 * b] = off_b;
+      a.piece_meta[2 * b + 1] = n_bal;
+    }
   }
 
   // Queries of the G heads sharing KV head g, in this lane's element order.
@@ -402,7 +466,8 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
   } else {
     const int S = a.ws_stride;
     for (int gq = 0; gq < G; ++gq) {
-      const int64_t slot = ((int64_t)b * Hq + g * G + gq) * S + split;
+      const int64_t slot = balanced ? (int64_t)(off_b + split) * Hq + g * G + gq
+                                    : ((int64_t)b * Hq + g * G + gq) * S + split;
       float* wo = a.ws_o + slot * D;
       for (int jj = 0; jj < NCH; ++jj) {
         const int d0 = (jj * TL + c) * EPC;
@@ -428,16 +493,30 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(RowAttnArgs a) {
   const int Hq = a.num_q_heads;
   if (pair >= a.num_seqs * Hq) return;
   const int b = pair / Hq;
-  const int L = a.context_lens[b];
-  const int start = a.kv_start ? a.kv_start[b] : 0;
-  const int ns = (L - start + a.split_tokens - 1) / a.split_tokens;
-  const int np = start > 0 ? (start + a.prefix_chunk - 1) / a.prefix_chunk : 0;
+  const int h = pair % Hq;
+  const bool balanced = a.balance_pieces > 0;
+  int ns, np = 0, first = 0;
+  if (balanced) {
+    // written by the first piece of the sequence in the split pass
+    first = a.piece_meta[2 * b];
+    ns = a.piece_meta[2 * b + 1];
+  } else {
+    const int L = a.context_lens[b];
+    const int start = a.kv_start ? a.kv_start[b] : 0;
+    ns = (L - start + a.split_tokens - 1) / a.split_tokens;
+    np = start > 0 ? (start + a.prefix_chunk - 1) / a.prefix_chunk : 0;
+  }
   if (np == 0 && ns <= 1) return;
   const int S = a.ws_stride;
-  const float* ml = a.ws_ml + (int64_t)pair * S * 2;
-  const float* wo = a.ws_o + (int64_t)pair * S * D + lane * EPL;
-  // slot of the i-th state: splits 0 .. ns-1, then prefix chunks at num_splits ..
-  auto slot = [&](int i) { return i < ns ? i : a.num_splits + (i - ns); };
+  const float* ml = a.ws_ml;
+  const float* wo = a.ws_o + lane * EPL;
+  // state of the i-th merged term: balanced pieces first .. first + ns - 1 of
+  // the sequence; else the pair's splits 0 .. ns-1, then its prefix chunks at
+  // num_splits ..
+  auto slot = [&](int i) -> int64_t {
+    if (balanced) return (int64_t)(first + i) * Hq + h;
+    return (int64_t)pair * S + (i < ns ? i : a.num_splits + (i - ns));
+  };
   // States are read kBatch at a time, so that their loads are in flight
   // together (the first batch's with the maxima of the rest: one memory round
   // trip for up to kBatch states); they are combined one by one in slot order.
@@ -447,11 +526,11 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(RowAttnArgs a) {
   auto load_batch = [&](int i0) {
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      const int j = slot(min(i0 + k, n - 1));  // past the end: the last state again, unused
+      const int64_t j = slot(min(i0 + k, n - 1));  // past the end: the last state again, unused
       mv[k] = ml[2 * j];
       lv[k] = ml[2 * j + 1];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) ov[k][e] = wo[(int64_t)j * D + e];
+      for (int e = 0; e < EPL; ++e) ov[k][e] = wo[j * D + e];
     }
   };
   load_batch(0);

@@ -76,7 +76,13 @@ def test_workspace_and_split_queries():
     assert L.pkv_decode_workspace_bytes(4, 8, 128, 300, 128) == 4 * 8 * 3 * 130 * 4
     for B, Hkv, maxL in [(256, 8, 1024), (64, 8, 8192), (200, 8, 32768), (4, 2, 100), (1, 1, 1)]:
         s = L.pkv_decode_split_tokens(B, Hkv * 4, Hkv, 128, maxL, 256, 1)
-        assert s > 0 and s % 64 == 0
+        assert (s > 0 and s % 64 == 0) or s == pkv.SPLIT_BALANCED
+    # token-balanced pieces: about 1024 pieces (at least one per sequence) of
+    # states, then two ints of piece bounds per sequence
+    assert L.pkv_decode_workspace_bytes(4, 8, 128, 100, pkv.SPLIT_BALANCED) == 1024 * 8 * 130 * 4 + 4 * 8
+    assert L.pkv_decode_workspace_bytes(1500, 4, 64, 9, pkv.SPLIT_BALANCED) == 1500 * 4 * 66 * 4 + 1500 * 8
+    # other negative splits are rejected before anything else is looked at
+    assert _dec(L, maxL=1000, split=-2) == -1
 
 
 @needs_lib

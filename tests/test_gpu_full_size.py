@@ -238,7 +238,7 @@ def long_f32():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("split", [0, 2048, 512])
+@pytest.mark.parametrize("split", [0, 2048, 512, pkv.SPLIT_BALANCED])
 def test_long_context_decode_fp32(long_f32, split):
     w, s, ref = long_f32
     assert int(w.dec_context_lens.max()) > 30000

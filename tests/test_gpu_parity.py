@@ -51,7 +51,7 @@ DECODE_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("split", [0, 64])
+@pytest.mark.parametrize("split", [0, 64, pkv.SPLIT_BALANCED])
 @pytest.mark.parametrize("shape", DECODE_SHAPES, ids=lambda s: "-".join(map(str, s)))
 def test_decode_tiny_sweep(shape, split):
     dtype, hq, hkv, d, bs = shape
@@ -213,6 +213,35 @@ def test_config3_long_decode_splitk(dtype):
     assert err <= tol(w.dtype), err
 
 
+@pytest.mark.parametrize("config", [2, 3])
+@pytest.mark.parametrize("dtype", [None, "f32"])
+def test_balanced_pieces_full_configs(config, dtype):
+    """Token-balanced pieces (about 1024 per launch, cut across the batch) on
+    the Qwen3-shaped and long-context decode workloads, every row."""
+    w = W.make_config(config, dtype=dtype)
+    log(f"config {config} dtype={w.dtype} balanced pieces")
+    step = DeviceStep(w)
+    step.step(split_tokens=pkv.SPLIT_BALANCED)
+    kc, vc = _check_store(step, w)
+    err = max_abs(to_host(step.dec_out, w.dtype), oracle_decode(w, kc, vc), w.dtype)
+    log(f"config {config} balanced max abs error {err:.3g}")
+    assert err <= tol(w.dtype), err
+
+
+def test_balanced_pieces_more_sequences_than_pieces():
+    """1100 sequences and about 1024 pieces: every sequence is one piece and
+    writes its output in the first pass; plus one long sequence, cut in many."""
+    rng = np.random.default_rng(16)
+    lens = [int(x) for x in rng.integers(1, 300, size=1100)] + [5000]
+    w = _decode_case("f32", 8, 2, 64, 16, lens, seed=16)
+    log("balanced pieces, 1101 sequences")
+    step = DeviceStep(w)
+    step.step(split_tokens=pkv.SPLIT_BALANCED)
+    kc, vc = _check_store(step, w)
+    err = max_abs(to_host(step.dec_out, "f32"), oracle_decode(w, kc, vc), "f32")
+    assert err <= 1e-5, err
+
+
 # The prefix-cached prefill and mixed-step workloads are compared row by row in
 # test_gpu_full_size.py.
 
@@ -282,14 +311,15 @@ def test_split_paths_agree():
         assert max_abs(o, ref, "f32") <= 1e-5
 
 
-def test_zero_length_context_gives_zeros():
+@pytest.mark.parametrize("split", [0, pkv.SPLIT_BALANCED])
+def test_zero_length_context_gives_zeros(split):
     w = _decode_case("bf16", 16, 8, 128, 16, [5, 7], seed=15)
     step = DeviceStep(w)
     step.store()
     cl = torch.tensor([0, 7], dtype=torch.int32, device="cuda")
     step.dec_out.fill_(1.0)
     pkv.paged_decode_attn(step.dec_q, step.k_cache, step.v_cache, step.dec_bt, cl, w.scale, step.dec_out,
-                          max_context_len=7)
+                          max_context_len=7, split_tokens=split)
     torch.cuda.synchronize()
     got = to_host(step.dec_out, "bf16")
     assert (got[0] == 0).all()
