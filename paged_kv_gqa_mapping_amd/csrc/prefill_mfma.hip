@@ -105,9 +105,9 @@ __device__ __forceinline__ void run_item(const PrefillArgs& a, uint8_t* lds, con
   // Q^T first: its loads are in flight while the first block ids (scalar
   // loads) arrive and the first tile's copies are issued
   wt.load_q(a.q, q_row, col_valid, ln.half);
-  src.fetch(blk, 0, ln.wave, lbs);
+  src.fetch(blk, 0, ln, lbs);
   src.issue(a, lds, ln, blk, 0, 0, 0);
-  if (n_kt > 1) src.fetch(blk, 1, ln.wave, lbs);
+  if (n_kt > 1) src.fetch(blk, 1, ln, lbs);
   wt.settle_q();
 
   // Pipeline: tile kt+1 is in flight (direct to LDS) while tile kt is
@@ -134,7 +134,7 @@ __device__ __forceinline__ void run_item(const PrefillArgs& a, uint8_t* lds, con
         }
       }
       // the next block ids arrive while this wave waits at the next barrier
-      if (kt + 2 < n_kt) src.fetch(blk, kt + 2, ln.wave, lbs);
+      if (kt + 2 < n_kt) src.fetch(blk, kt + 2, ln, lbs);
       const int v_free = vprev;
       vprev = vcur;
       vcur = vnext;
@@ -144,7 +144,67 @@ __device__ __forceinline__ void run_item(const PrefillArgs& a, uint8_t* lds, con
     if constexpr (is_late)
       if (n_kt_wave == n_kt && n_kt > 0) wt.template pv<false>(lds, ln, vprev);
   };
-  if (kSkew && ln.wave >= kWaves / 2)
+  // Ping-pong: waves 0-3 (group E, one per SIMD) and 4-7 (group L) alternate
+  // between their products and their softmax, so that in each segment one
+  // wave of a SIMD keeps its matrix core busy while the other computes the
+  // exponentials.  Tile kt:
+  //   segment A: E: O^T += V(kt-1) P(kt-1)^T, S(kt) = K(kt) Q^T;
+  //              L: softmax of S(kt-1), then the copies of K(kt+1)
+  //   segment B: E: softmax of S(kt), then the copies of V(kt+1);
+  //              L: O^T += V(kt-1) P(kt-1)^T, S(kt) = K(kt) Q^T
+  // with one more tile (kt = n_kt) for the last P V product.  K tiles use two
+  // buffers (K(kt+1) goes where K(kt-1) was, whose readers finished before
+  // barrier A of tile kt), V tiles three (V(kt+1) goes where V(kt-2) was).
+  // At barrier A each L wave has waited for its copies of K(kt) and each E
+  // wave for its copies of V(kt-1) (those of V(kt), issued one segment later,
+  // may still be in flight: vector memory operations complete in order).
+  // The two groups run separate copies of the loop (the same barriers in the
+  // same order), so that each keeps only its own values live.
+  auto pingpong = [&](auto GROUP_E) __attribute__((always_inline)) {
+    constexpr bool is_e = decltype(GROUP_E)::value;
+    f32x16_t acc_s[kKB];
+    int vprev = kVBufs - 1, vnext = 1 % kVBufs;  // V buffers of tiles kt-1 and kt+1
+    auto copies = [&](int kt) __attribute__((always_inline)) {
+      if (kt + 1 < n_kt) {
+        src.issue(a, lds, ln, blk, kt + 1, (kt + 1) & 1, vnext);
+        if (kt + 2 < n_kt) src.fetch(blk, kt + 2, ln, lbs);
+      }
+    };
+    auto products = [&](int kt) __attribute__((always_inline)) {
+      if (kt >= 1 && kt - 1 < n_kt_wave) wt.template pv<false>(lds, ln, vprev);
+      if (kt < n_kt_wave) wt.template qk<false>(lds, ln, kt & 1, 0, acc_s);
+    };
+    for (int kt = 0; kt <= n_kt; ++kt) {
+      if (is_e && kt >= 1 && kt < n_kt)
+        wait_vmem<Gm::IPW>();
+      else
+        wait_vmem<0>();
+      __syncthreads();
+      if constexpr (is_e) {
+        products(kt);
+      } else {
+        if (kt >= 1 && kt - 1 < n_kt_wave) wt.softmax(ln, acc_s, (kt - 1) * kKT, pos, min_pos, c);
+        copies(kt);
+      }
+      __syncthreads();
+      if constexpr (is_e) {
+        if (kt < n_kt_wave) wt.softmax(ln, acc_s, kt * kKT, pos, min_pos, c);
+        copies(kt);
+      } else {
+        products(kt);
+      }
+      // V buffers: tile kt's becomes the previous one, tile kt+2's takes the
+      // oldest (that of tile kt-1)
+      const int v_kt = vprev == kVBufs - 1 ? 0 : vprev + 1;
+      vnext = vprev;
+      vprev = v_kt;
+    }
+  };
+  if (kPingPong && ln.vpart)
+    pingpong(std::true_type{});
+  else if (kPingPong)
+    pingpong(std::false_type{});
+  else if (kSkew && ln.wave >= kWaves / 2)
     tile_loop(std::true_type{});
   else
     tile_loop(std::false_type{});
@@ -241,13 +301,13 @@ __device__ __forceinline__ const_i32_t* item_record(const PrefillArgs& a, int xc
 
 // The part of an item the stream keeps in scalar registers: its key tiles
 // [kt_lo, kt_hi), and for this wave the block's first position and the end of
-// the key tiles it computes; per lane, each column's position (the last key
-// past the sequence's queries) and row of q and out (times Hq, plus the head;
-// -1 past the queries).  The rest of the record (piece, split) is read again
-// when the item ends.
+// the key tiles it computes; per lane, each column's row of q and out (times
+// Hq, plus the head; -1 past the queries).  Column col's position is
+// min_pos + col (past the sequence's queries the column's output is not
+// written, so its position does not matter).  The rest of the record (piece,
+// split) is read again when the item ends.
 struct Item2 {
   int kt_lo, kt_hi, min_pos, n_kt_wave;
-  int pos;
   int64_t q_row;
   __device__ __forceinline__ bool valid() const { return q_row >= 0; }
 };
@@ -276,7 +336,6 @@ __device__ __forceinline__ void load_item(const PrefillArgs& a, int xcd, int idx
   const int qi = first + col;
   const int shift = Lk - Lq;
   const bool valid = qi < Lq;
-  x.pos = valid ? shift + qi : Lk - 1;
   x.q_row = valid ? (int64_t)(q0 + qi) * Hq + head : -1;
   x.min_pos = shift + first;
   const int w_max_pos = first < Lq ? shift + min(first + 32, Lq) - 1 : -1;
@@ -435,7 +494,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_stream_kernel(PrefillArgs
     int32_t blk[Gm::NBLK];
 #pragma unroll
     for (int j = 0; j < Gm::NBLK; ++j) blk[j] = 0;
-    src_cur.fetch(blk, cur.kt_lo, ln.wave, lbs);
+    src_cur.fetch(blk, cur.kt_lo, ln, lbs);
     src_cur.issue(a, lds, ln, blk, cur.kt_lo, 0, 0);
     int csel = 0, ct = cur.kt_lo + 1;
     if (ct >= cur.kt_hi) {
@@ -444,9 +503,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_stream_kernel(PrefillArgs
     }
     auto prefetch_blocks = [&]() __attribute__((always_inline)) {
       if (csel == 0)
-        src_cur.fetch(blk, ct, ln.wave, lbs);
+        src_cur.fetch(blk, ct, ln, lbs);
       else if (csel == 1)
-        src_nxt.fetch(blk, ct, ln.wave, lbs);
+        src_nxt.fetch(blk, ct, ln, lbs);
     };
     prefetch_blocks();
 
@@ -498,10 +557,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_stream_kernel(PrefillArgs
       // compute tile kt of cur
       if constexpr (is_late) {
         if (kt > cur.kt_lo && kt <= cur.n_kt_wave) wt.template pv<false>(lds, ln, vprev);
-        if (kt < cur.n_kt_wave) wt.template qk_softmax<false>(lds, ln, gt & 1, kt * kKT, 0, cur.pos, cur.min_pos, c);
+        if (kt < cur.n_kt_wave) wt.template qk_softmax<false>(lds, ln, gt & 1, kt * kKT, 0, cur.min_pos + ln.col, cur.min_pos, c);
       } else {
         if (kt < cur.n_kt_wave) {
-          wt.template qk_softmax<true>(lds, ln, gt & 1, kt * kKT, vcur, cur.pos, cur.min_pos, c);
+          wt.template qk_softmax<true>(lds, ln, gt & 1, kt * kKT, vcur, cur.min_pos + ln.col, cur.min_pos, c);
           if (!last) wt.template pv<true>(lds, ln, vcur);
         }
       }

@@ -52,6 +52,15 @@ constexpr int kCB = 8;         // column blocks per workgroup
 #define PKV_PREFILL_SKEW 1
 #endif
 constexpr bool kSkew = PKV_PREFILL_SKEW != 0;
+// Ping-pong schedule (one-launch and shared-prefix kernels): each tile has two
+// segments split by barriers; on every SIMD one wave runs its matrix products
+// while the other runs its softmax and issues its copies, and the roles swap
+// at the next segment.
+#ifndef PKV_PREFILL_PINGPONG
+#define PKV_PREFILL_PINGPONG 0
+#endif
+constexpr bool kPingPong = PKV_PREFILL_PINGPONG != 0;
+static_assert(!kPingPong || kSkew, "the ping-pong schedule keeps three V tile buffers");
 // Compile-time tuning knobs (defaults are the measured choice): LDS fragment
 // reads in flight ahead of the MFMAs (K, V^T), and the wave priority taken
 // while a wave issues its matrix products (0: never raised).
@@ -72,15 +81,9 @@ constexpr int kVBufs = kSkew ? 3 : 2;  // V tile buffers in LDS
 constexpr int kXcds = 8;  // accelerator dies (XCDs), each with its own L2
 constexpr int kWaves = kCB;
 constexpr int kThreads = 64 * kWaves;
-// Waves that copy the K/V tiles (the first kCopiers; the others only read
-// them).  With 4, the copies are issued by the early waves, which would
-// otherwise wait at the next barrier for the late ones, while the late waves
-// start their products at once.
-#ifndef PKV_PREFILL_COPIERS
-#define PKV_PREFILL_COPIERS 8
-#endif
-constexpr int kCopiers = PKV_PREFILL_COPIERS;
-static_assert(kCopiers == 8 || kCopiers == 4, "copier waves: all or the early half");
+// Tile copies: the 128 rows of a tile are 4 row groups of 32; wave w copies
+// row group w % 4 of the V tile (waves 0-3) or of the K tile (waves 4-7).
+constexpr int kRowGroups = 4;
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
@@ -127,8 +130,8 @@ struct Geom {
   static constexpr int CPR = D / 8;                   // 16-byte slots per row
   static constexpr int TILEB = kKT * ROWB;            // bytes per K (or V) tile
   static constexpr int RPI = 1024 / ROWB;             // rows per copy instruction (4 or 8)
-  static constexpr int RW = kKT / kCopiers;           // rows of each tile copied by one copier wave
-  static constexpr int IPW = RW / RPI;                // copy instructions per wave, tile and tensor
+  static constexpr int RW = kKT / kRowGroups;         // rows of a tile copied by one wave (its row group)
+  static constexpr int IPW = RW / RPI;                // copy instructions per wave and tile
   static constexpr int NBLK = RW / 8;                 // block ids per wave and tile (groups of 8 rows)
   static constexpr int KR = kKB * KSTEPS;             // K fragment reads per tile
   static constexpr int VR = kKT / 16 * MD;            // V^T fragments per tile (two transposing reads each)
@@ -148,9 +151,11 @@ template <int D>
 struct Lanes {
   using Gm = Geom<D>;
   int wave, lane, col, half;
+  int rgroup;  // row group this wave copies
+  bool vpart;  // it copies V rows (else K rows)
   uint32_t koff[Gm::KSTEPS];
   uint32_t voff[Gm::MD];
-  uint32_t src[2 * Gm::IPW];  // row within the instruction (times the row pitch, added per item) and rotated slot
+  uint32_t src[Gm::IPW];  // row within the instruction (times the row pitch, added per item) and rotated slot
 
   __device__ __forceinline__ void init(int32_t num_kv_heads) {
     const int tid = threadIdx.x;
@@ -159,6 +164,8 @@ struct Lanes {
     lane = tid & 63;
     col = lane & 31;
     half = lane >> 5;
+    rgroup = wave % kRowGroups;
+    vpart = wave < kRowGroups;
     // K (A operand of S^T): lane (col, half), step kk: key row col (+ 32 mb, which
     // keeps the rotation), chunk 2 kk + half.
 #pragma unroll
@@ -176,41 +183,42 @@ struct Lanes {
       for (int md = 0; md < Gm::MD; ++md)
         voff[md] = (4 * half + (r >> 2)) * Gm::ROWB + 16 * ((4 * md + qr) & (Gm::CPR - 1)) + 8 * (r & 1);
     }
-    // copy instruction i (K for i < IPW, then V) fills row lr of its RPI rows,
-    // slot ls of the row, holding the rotated chunk ch
+    // copy instruction i fills row lr of its RPI rows, slot ls of the row,
+    // holding the rotated chunk ch
     const int lr = lane / Gm::CPR;
     const int ls = lane % Gm::CPR;
     const uint32_t row_bytes = (uint32_t)num_kv_heads * Gm::ROWB;
 #pragma unroll
-    for (int i = 0; i < 2 * Gm::IPW; ++i) {
-      const int rt = Gm::RW * wave + (i % Gm::IPW) * Gm::RPI + lr;
-      const int ch = i >= Gm::IPW ? (ls - vrot<D>(rt)) & (Gm::CPR - 1) : (ls - rt) & (Gm::CPR - 1);
+    for (int i = 0; i < Gm::IPW; ++i) {
+      const int rt = Gm::RW * rgroup + i * Gm::RPI + lr;
+      const int ch = vpart ? (ls - vrot<D>(rt)) & (Gm::CPR - 1) : (ls - rt) & (Gm::CPR - 1);
       src[i] = lr * row_bytes + 16 * ch;
     }
   }
 };
 
+// a hook that does nothing
+struct NoHook {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
 // One wave's copies of one tile: where every row the wave copies exists
 // (`whole`), the byte offsets (in the pool, head included) of its groups of 8
-// rows, each group in one block, and issue(i) issues copy instruction i (K for
-// i < IPW, then V) from them with two scalar additions; otherwise the copies
-// were issued when the tile was planned and issue(i) does nothing.
+// rows, each group in one block, and issue(i) issues copy instruction i from
+// them with two scalar additions; otherwise the copies were issued when the
+// tile was planned and issue(i) does nothing.
 template <int D>
 struct TileCopy {
   using Gm = Geom<D>;
   int64_t off[Gm::NBLK];
   bool whole;
 
-  __device__ __forceinline__ void issue(const PrefillArgs& a, uint8_t* lds, const Lanes<D>& ln, int kb, int vb,
-                                        int i) const {
-    if (!whole || ln.wave >= kCopiers) return;
-    const int ii = i % Gm::IPW;
-    const bool is_v = i >= Gm::IPW;
-    const uint32_t dst = uniform(lds_addr(&lds[(is_v ? kKBufs + vb : kb) * Gm::TILEB]) +
-                                 Gm::RW * ln.wave * Gm::ROWB + ii * 1024);
-    const uint8_t* bytes = (const uint8_t*)(is_v ? a.v : a.k);
+  // dst: LDS byte address of the wave's rows in the destination buffer
+  __device__ __forceinline__ void issue(const PrefillArgs& a, const Lanes<D>& ln, uint32_t dst, int i) const {
+    if (!whole) return;
+    const uint8_t* bytes = (const uint8_t*)(ln.vpart ? a.v : a.k);
     const int64_t row_bytes = (int64_t)a.num_kv_heads * Gm::ROWB;
-    copy_to_lds(bytes + off[(ii * Gm::RPI) / 8] + ((ii * Gm::RPI) % 8) * row_bytes, ln.src[i], dst);
+    copy_to_lds(bytes + off[(i * Gm::RPI) / 8] + ((i * Gm::RPI) % 8) * row_bytes, ln.src[i], uniform(dst + i * 1024));
   }
 };
 
@@ -235,45 +243,49 @@ struct TileSource {
     head_bytes = (uint32_t)g * Gm::ROWB;
   }
 
-  // block ids of tile t's rows copied by this wave: rows RW w + 8 j .. + 7 lie in
-  // one block (block_size >= 8), one id per group j of 8 rows (the same block for
-  // both groups of 16 rows unless block_size is 8)
-  __device__ __forceinline__ void fetch(int32_t (&blk)[Gm::NBLK], int t, int wave, int lbs) const {
-    if (!table || wave >= kCopiers) return;
+  // block ids of tile t's rows copied by this wave: rows RW r + 8 j .. + 7 of
+  // row group r lie in one block (block_size >= 8), one id per group j of 8 rows
+  __device__ __forceinline__ void fetch(int32_t (&blk)[Gm::NBLK], int t, const Lanes<D>& ln, int lbs) const {
+    if (!table) return;
 #pragma unroll
     for (int j = 0; j < Gm::NBLK; ++j)
-      blk[j] = table[uniform((key_base + min(t * kKT + Gm::RW * wave + 8 * j, last_key)) >> lbs)];
+      blk[j] = table[uniform((key_base + min(t * kKT + Gm::RW * ln.rgroup + 8 * j, last_key)) >> lbs)];
   }
 
-  // Copy instructions of tile t into K buffer kb and V buffer vb (absolute LDS
-  // buffer indices): wave w copies rows RW w .. RW w + RW - 1 of each K and V
-  // tile (IPW instructions each, RPI rows per instruction); lane L of an
-  // instruction fills slot L % CPR of row L / CPR.  The RPI rows of one
-  // instruction start at a multiple of RPI, so they lie in one block; on a tile
-  // that reaches past the last key (whose rows then clamp to it) each lane
-  // computes its own row.
+  // LDS byte address of this wave's rows in K buffer kb or V buffer vb (its part)
+  __device__ __forceinline__ static uint32_t dst_of(uint8_t* lds, const Lanes<D>& ln, int kb, int vb) {
+    return lds_addr(&lds[(ln.vpart ? kKBufs + vb : kb) * Gm::TILEB]) + Gm::RW * ln.rgroup * Gm::ROWB;
+  }
+
+  // Copies of tile t into K buffer kb or V buffer vb (absolute LDS buffer
+  // indices): this wave's row group of its part (IPW instructions of RPI rows;
+  // lane L of an instruction fills slot L % CPR of row L / CPR).  The RPI rows
+  // of one instruction start at a multiple of RPI, so they lie in one block;
+  // on a tile that reaches past the last key (whose rows then clamp to it)
+  // each lane computes its own row.
   __device__ __forceinline__ void issue(const PrefillArgs& a, uint8_t* lds, const Lanes<D>& ln,
                                         const int32_t (&blk)[Gm::NBLK], int t, int kb, int vb) const {
     const TileCopy<D> tc = plan(a, lds, ln, blk, t, kb, vb);
+    const uint32_t dst = dst_of(lds, ln, kb, vb);
 #pragma unroll
-    for (int i = 0; i < 2 * Gm::IPW; ++i) tc.issue(a, lds, ln, kb, vb, i);
+    for (int i = 0; i < Gm::IPW; ++i) tc.issue(a, ln, dst, i);
   }
 
-  // The copies of tile t for one wave.  Where every row the wave copies exists,
-  // they are left to TileCopy::issue; a tile that reaches past the last key is
-  // copied here, with per-lane row addresses.
+  // The copies of tile t for this wave.  Where every row the wave copies
+  // exists, they are left to TileCopy::issue; a tile that reaches past the
+  // last key is copied here, with per-lane row addresses.
   __device__ __forceinline__ TileCopy<D> plan(const PrefillArgs& a, uint8_t* lds, const Lanes<D>& ln,
                                               const int32_t (&blk)[Gm::NBLK], int t, int kb, int vb) const {
     TileCopy<D> tc;
     const int lbs = a.log2_block_size;
     const int bs_mask = (1 << lbs) - 1;
     const int64_t row_bytes = (int64_t)a.num_kv_heads * Gm::ROWB;
-    tc.whole = t * kKT + Gm::RW * ln.wave + Gm::RW - 1 <= last_key;  // every row this wave copies exists
-    if (ln.wave >= kCopiers) return tc;
-    // rows RW w + 8 j .. + 7 of the tile: one block, consecutive rows in it
+    const int r0 = t * kKT + Gm::RW * ln.rgroup;  // first row (in the item) this wave copies
+    tc.whole = r0 + Gm::RW - 1 <= last_key;
+    // rows r0 + 8 j .. + 7: one block, consecutive rows in it
 #pragma unroll
     for (int j = 0; j < Gm::NBLK; ++j) {
-      const int rj = t * kKT + Gm::RW * ln.wave + 8 * j;
+      const int rj = r0 + 8 * j;
       const int64_t row = table ? ((int64_t)blk[j] << lbs) + ((key_base + rj) & bs_mask) : (int64_t)(k0 + rj);
       tc.off[j] = row * row_bytes + head_bytes;
     }
@@ -281,20 +293,17 @@ struct TileSource {
     const int lr = ln.lane / Gm::CPR;
     const int ls = ln.lane % Gm::CPR;
     const int64_t blk_bytes = row_bytes << lbs;
+    const uint32_t dst = dst_of(lds, ln, kb, vb);
+    const uint8_t* bytes = (const uint8_t*)(ln.vpart ? a.v : a.k);
 #pragma unroll
-    for (int i = 0; i < 2 * Gm::IPW; ++i) {
-      const int ii = i % Gm::IPW;
-      const bool is_v = i >= Gm::IPW;
-      const uint32_t dst = uniform(lds_addr(&lds[(is_v ? kKBufs + vb : kb) * Gm::TILEB]) +
-                                   Gm::RW * ln.wave * Gm::ROWB + ii * 1024);
-      const uint8_t* bytes = (const uint8_t*)(is_v ? a.v : a.k);
-      const int rt = Gm::RW * ln.wave + ii * Gm::RPI + lr;  // row within the tile
+    for (int i = 0; i < Gm::IPW; ++i) {
+      const int rt = Gm::RW * ln.rgroup + i * Gm::RPI + lr;  // row within the tile
       const int tcl = min(t * kKT + rt, last_key);
-      const int64_t row = table ? (int64_t)blk[(ii * Gm::RPI) / 8] * blk_bytes +
+      const int64_t row = table ? (int64_t)blk[(i * Gm::RPI) / 8] * blk_bytes +
                                       (int64_t)((key_base + tcl) & bs_mask) * row_bytes
                                 : (int64_t)(k0 + tcl) * row_bytes;
-      const int ch = is_v ? (ls - vrot<D>(rt)) & (Gm::CPR - 1) : (ls - rt) & (Gm::CPR - 1);
-      copy_to_lds(bytes + row + head_bytes + 16 * ch, dst);
+      const int ch = ln.vpart ? (ls - vrot<D>(rt)) & (Gm::CPR - 1) : (ls - rt) & (Gm::CPR - 1);
+      copy_to_lds(bytes + row + head_bytes + 16 * ch, uniform(dst + i * 1024));
     }
     return tc;
   }
@@ -352,21 +361,24 @@ struct WaveTile {
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 
-  // S^T = K Q^T (raw scores) for K buffer kb, then the online softmax, which
-  // leaves the bf16 weights in pw.  The K fragment reads run kKPF ahead of the
-  // MFMAs.  With PRE, the first V^T fragments of V buffer vb are requested at
-  // the end of the products, so that they arrive during the softmax.  Column
-  // position pos sees keys <= pos; the mask is applied only on tiles that reach
-  // past the block's first position min_pos.  c = scale * log2(e) > 0.
+  // S^T = K Q^T for K buffer kb, then the online softmax (both below).
   template <bool PRE>
   __device__ __forceinline__ void qk_softmax(const uint8_t* lds, const Lanes<D>& ln, int kb, int key0, int vb, int pos,
                                              int min_pos, float c) {
+    f32x16_t acc_s[kKB];
+    qk<PRE>(lds, ln, kb, vb, acc_s);
+    softmax(ln, acc_s, key0, pos, min_pos, c);
+  }
+
+  // S^T = K Q^T (raw scores, one 32-key block each) for K buffer kb into acc_s, the K fragment reads
+  // kKPF ahead of the MFMAs; with PRE, the first V^T fragments of V buffer vb
+  // are requested at the end, so that they arrive during the softmax.
+  template <bool PRE>
+  __device__ __forceinline__ void qk(const uint8_t* lds, const Lanes<D>& ln, int kb, int vb, f32x16_t (&acc_s)[kKB]) {
     constexpr int kSchedMfma = 0x008;
     constexpr int kSchedDsRead = 0x100;
     constexpr int kKPF = PKV_PREFILL_KPF;
     constexpr int kVPF = PKV_PREFILL_VPF;
-    const int half = ln.half;
-    f32x16_t acc_s[kKB];
 #pragma unroll
     for (int mb = 0; mb < kKB; ++mb)
 #pragma unroll
@@ -393,7 +405,18 @@ struct WaveTile {
     }
     if constexpr (PRE) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * kVPF, 0);
     if constexpr (PKV_PREFILL_PRIO_QK > 0) __builtin_amdgcn_s_setprio(0);
+  }
 
+  // The online softmax of the scores in acc_s (keys key0 ..), which leaves the
+  // bf16 weights in pw.  Column position pos sees keys <= pos; the mask is
+  // applied only on tiles that reach past the block's first position min_pos.
+  // c = scale * log2(e) > 0.
+  // hook(i) runs after the weights of keys 4i .. 4i+3 (i < 32) are made: the
+  // ping-pong schedule issues its tile copies there, spread over the softmax.
+  template <typename Hook = NoHook>
+  __device__ __forceinline__ void softmax(const Lanes<D>& ln, f32x16_t (&acc_s)[kKB], int key0, int pos, int min_pos,
+                                          float c, const Hook& hook = Hook()) {
+    const int half = ln.half;
     // causal mask (only on tiles that reach past the block's first position):
     // key key0 + off(r) with off(r) = mb*32 + (r/4)*8 + half*4 + r%4 is
     // visible iff off(r) - half*4 <= pos - key0 - half*4
@@ -403,7 +426,12 @@ struct WaveTile {
       for (int mb = 0; mb < kKB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
+        {
           if (mb * 32 + (r >> 2) * 8 + (r & 3) > lim) acc_s[mb][r] = kNegInf;
+          // one compare and select at a time: hoisted together, the 64 lane
+          // masks would fill the scalar registers
+          __builtin_amdgcn_sched_barrier(0);
+        }
     }
     float mx = kNegInf;
 #pragma unroll
@@ -429,6 +457,7 @@ struct WaveTile {
       const float s1 = acc_s[i >> 3][(2 * i + 1) & 15];
       pw[i] = pack_bf16x2(exp2_hw(fmaf(s0, c, -m)), exp2_hw(fmaf(s1, c, -m)));
       lsum = dot2_bf16(pw[i], kOnes, lsum);
+      hook(i);
     }
   }
 
