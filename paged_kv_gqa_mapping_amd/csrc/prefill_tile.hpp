@@ -43,6 +43,7 @@ namespace pf {
 // computed, ahead by a tile's compute time.
 constexpr int kKT = 128;
 constexpr int kKB = kKT / 32;  // 32-key blocks per tile
+static_assert(kKB == 4, "the softmax joins four per-block chains");
 constexpr int kCB = 8;         // column blocks per workgroup
 // Skewed schedule: waves 4-7 (which share SIMDs with waves 0-3) multiply a
 // tile's weights by V one tile later, after the next barrier, so that the two
@@ -433,11 +434,17 @@ struct WaveTile {
           __builtin_amdgcn_sched_barrier(0);
         }
     }
-    float mx = kNegInf;
+    // the column max, as kKB independent chains (one per key block) joined at the end
+    float bmx[kKB];
 #pragma unroll
-    for (int mb = 0; mb < kKB; ++mb)
+    for (int mb = 0; mb < kKB; ++mb) {
+      bmx[mb] = acc_s[mb][0];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc_s[mb][r]);
+      for (int r = 1; r < 16; ++r) bmx[mb] = fmaxf(bmx[mb], acc_s[mb][r]);
+    }
+    float mx = bmx[0];
+#pragma unroll
+    for (int mb = 1; mb < kKB; ++mb) mx = fmaxf(mx, bmx[mb]);
     mx = halves_max(mx) * c;  // c > 0, so the max commutes with the scaling
     if (wave_any(mx > m + kTau)) {
       const float mn = fmaxf(m, mx);
@@ -449,16 +456,22 @@ struct WaveTile {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc_o[md][r] *= alpha;
     }
-    // P^T = 2^(c s - m), rounded to bf16, as the B operand of the 16-key steps
+    // P^T = 2^(c s - m), rounded to bf16, as the B operand of the 16-key steps;
+    // the weight sum in kKB independent chains (one per key block), added to
+    // the running sum at the end
     const uint32_t kOnes = 0x3F803F80u;  // bf16 pair (1, 1)
+    float bl[kKB];
+#pragma unroll
+    for (int mb = 0; mb < kKB; ++mb) bl[mb] = 0.f;
 #pragma unroll
     for (int i = 0; i < kKT / 4; ++i) {
       const float s0 = acc_s[i >> 3][(2 * i) & 15];
       const float s1 = acc_s[i >> 3][(2 * i + 1) & 15];
       pw[i] = pack_bf16x2(exp2_hw(fmaf(s0, c, -m)), exp2_hw(fmaf(s1, c, -m)));
-      lsum = dot2_bf16(pw[i], kOnes, lsum);
+      bl[i >> 3] = dot2_bf16(pw[i], kOnes, bl[i >> 3]);
       hook(i);
     }
+    lsum += (bl[0] + bl[1]) + (bl[2] + bl[3]);
   }
 
   // O^T += V^T P^T for V buffer vb, V^T fragments read kVPF ahead (the first
