@@ -59,287 +59,15 @@ enum Mode { kGrid = 0, kShared = 1 };
 // [key_base, key_base + Lk) of its prefix, table row b.
 struct Item {
   int b, hg, tile, q0, Lq, k0, Lk, key_base, member0, chunk;
+  // a piece of a planned query tile: key tiles [kt_lo, kt_hi) (kt_hi < 0: all
+  // the tile needs); split >= 0: piece pc & 0xffff of pc >> 16, arrival
+  // counters from split * 8 and state slots from `slot`
+  int kt_lo = 0, kt_hi = -1, split = -1, slot = 0, pc = 0;
 };
-
-template <int D, int HW, int MODE>
-__device__ __forceinline__ void run_item(const PrefillArgs& a, uint8_t* lds, const Item& it) {
-  using Gm = Geom<D>;
-  constexpr bool SHARED = MODE == kShared;
-  constexpr int QP = 32 * (kCB / HW);  // positions (members) per workgroup
-  Lanes<D> ln;
-  ln.init(a.num_kv_heads);
-  const int Hq = a.num_q_heads;
-  const int G = Hq / a.num_kv_heads;
-  const int g = (it.hg * HW) / G;
-  // Positions are relative to key_base.  Prefill: query i sits at shift + i.
-  // Shared: every column sees the whole chunk, as a query at its last key.
-  const int shift = it.Lk - it.Lq;
-  // this wave's column block: head h, queries (members) first + col
-  const int h = it.hg * HW + ln.wave % HW;
-  const int first = it.tile * QP + 32 * (ln.wave / HW);
-  const int qi = first + ln.col;
-  const bool col_valid = qi < it.Lq;
-  const int pos = (col_valid && !SHARED) ? shift + qi : it.Lk - 1;
-  const int min_pos = SHARED ? it.Lk - 1 : shift + first;
-  const int w_max_pos = first < it.Lq ? (SHARED ? it.Lk - 1 : shift + min(first + 32, it.Lq) - 1) : -1;
-  int64_t q_row;  // row of q[., Hq, D] (times Hq, plus the head)
-  if constexpr (SHARED) {
-    q_row = col_valid ? (int64_t)a.group_seqs[it.member0 + qi] * Hq + h : 0;
-  } else {
-    q_row = (int64_t)(it.q0 + qi) * Hq + h;
-  }
-  const int wg_max_pos = SHARED ? it.Lk - 1 : shift + min(it.tile * QP + QP, it.Lq) - 1;
-  const int n_kt = wg_max_pos / kKT + 1;
-  const int n_kt_wave = w_max_pos >= 0 ? min(n_kt, w_max_pos / kKT + 1) : 0;
-
-  const int lbs = a.log2_block_size;
-  TileSource<D> src;
-  src.init(a, it.b, g, it.k0, it.key_base, it.Lk);
-  int32_t blk[Gm::NBLK];
-#pragma unroll
-  for (int j = 0; j < Gm::NBLK; ++j) blk[j] = 0;
-  WaveTile<D> wt;
-  wt.reset();
-  const float c = a.scale_log2;  // > 0
-
-  // Q^T first: its loads are in flight while the first block ids (scalar
-  // loads) arrive and the first tile's copies are issued
-  wt.load_q(a.q, q_row, col_valid, ln.half);
-  src.fetch(blk, 0, ln, lbs);
-  src.issue(a, lds, ln, blk, 0, 0, 0);
-  if (n_kt > 1) src.fetch(blk, 1, ln, lbs);
-  wt.settle_q();
-
-  // Pipeline: tile kt+1 is in flight (direct to LDS) while tile kt is
-  // computed; one barrier per tile.  At the barrier of tile kt each wave has
-  // waited for its own copies of tile kt (the only ones in flight) and every
-  // wave has finished its work on the buffers that the copies of tile kt+1
-  // overwrite: K of tile kt-1, and V of tile kt-1 (two buffers) or of tile
-  // kt-2 (three buffers, where the late waves still read V of tile kt-1 after
-  // the barrier).  V buffers of tiles kt - 1, kt and kt + 1 rotate each tile.
-  auto tile_loop = [&](auto LATE) __attribute__((always_inline)) {
-    constexpr bool is_late = decltype(LATE)::value;
-    int vprev = kVBufs - 1, vcur = 0, vnext = 1 % kVBufs;
-    for (int kt = 0; kt < n_kt; ++kt) {
-      wait_vmem<0>();
-      __syncthreads();
-      if (kt + 1 < n_kt) src.issue(a, lds, ln, blk, kt + 1, (kt + 1) & 1, vnext);
-      if constexpr (is_late) {
-        if (kt >= 1 && kt <= n_kt_wave) wt.template pv<false>(lds, ln, vprev);
-        if (kt < n_kt_wave) wt.template qk_softmax<false>(lds, ln, kt & 1, kt * kKT, 0, pos, min_pos, c);
-      } else {
-        if (kt < n_kt_wave) {
-          wt.template qk_softmax<true>(lds, ln, kt & 1, kt * kKT, vcur, pos, min_pos, c);
-          wt.template pv<true>(lds, ln, vcur);
-        }
-      }
-      // the next block ids arrive while this wave waits at the next barrier
-      if (kt + 2 < n_kt) src.fetch(blk, kt + 2, ln, lbs);
-      const int v_free = vprev;
-      vprev = vcur;
-      vcur = vnext;
-      vnext = kVBufs == 3 ? v_free : vprev;
-    }
-    // a late wave's last tile (no copies are in flight any more)
-    if constexpr (is_late)
-      if (n_kt_wave == n_kt && n_kt > 0) wt.template pv<false>(lds, ln, vprev);
-  };
-  // Ping-pong: waves 0-3 (group E, one per SIMD) and 4-7 (group L) alternate
-  // between their products and their softmax, so that in each segment one
-  // wave of a SIMD keeps its matrix core busy while the other computes the
-  // exponentials.  Tile kt:
-  //   segment A: E: O^T += V(kt-1) P(kt-1)^T, S(kt) = K(kt) Q^T;
-  //              L: softmax of S(kt-1), then the copies of K(kt+1)
-  //   segment B: E: softmax of S(kt), then the copies of V(kt+1);
-  //              L: O^T += V(kt-1) P(kt-1)^T, S(kt) = K(kt) Q^T
-  // with one more tile (kt = n_kt) for the last P V product.  K tiles use two
-  // buffers (K(kt+1) goes where K(kt-1) was, whose readers finished before
-  // barrier A of tile kt), V tiles three (V(kt+1) goes where V(kt-2) was).
-  // At barrier A each L wave has waited for its copies of K(kt) and each E
-  // wave for its copies of V(kt-1) (those of V(kt), issued one segment later,
-  // may still be in flight: vector memory operations complete in order).
-  // The two groups run separate copies of the loop (the same barriers in the
-  // same order), so that each keeps only its own values live.
-  auto pingpong = [&](auto GROUP_E) __attribute__((always_inline)) {
-    constexpr bool is_e = decltype(GROUP_E)::value;
-    f32x16_t acc_s[kKB];
-    int vprev = kVBufs - 1, vnext = 1 % kVBufs;  // V buffers of tiles kt-1 and kt+1
-    auto copies = [&](int kt) __attribute__((always_inline)) {
-      if (kt + 1 < n_kt) {
-        src.issue(a, lds, ln, blk, kt + 1, (kt + 1) & 1, vnext);
-        if (kt + 2 < n_kt) src.fetch(blk, kt + 2, ln, lbs);
-      }
-    };
-    auto products = [&](int kt) __attribute__((always_inline)) {
-      if (kt >= 1 && kt - 1 < n_kt_wave) wt.template pv<false>(lds, ln, vprev);
-      if (kt < n_kt_wave) wt.template qk<false>(lds, ln, kt & 1, 0, acc_s);
-    };
-    for (int kt = 0; kt <= n_kt; ++kt) {
-      if (is_e && kt >= 1 && kt < n_kt)
-        wait_vmem<Gm::IPW>();
-      else
-        wait_vmem<0>();
-      __syncthreads();
-      if constexpr (is_e) {
-        products(kt);
-      } else {
-        if (kt >= 1 && kt - 1 < n_kt_wave) wt.softmax(ln, acc_s, (kt - 1) * kKT, pos, min_pos, c);
-        copies(kt);
-      }
-      __syncthreads();
-      if constexpr (is_e) {
-        if (kt < n_kt_wave) wt.softmax(ln, acc_s, kt * kKT, pos, min_pos, c);
-        copies(kt);
-      } else {
-        products(kt);
-      }
-      // V buffers: tile kt's becomes the previous one, tile kt+2's takes the
-      // oldest (that of tile kt-1)
-      const int v_kt = vprev == kVBufs - 1 ? 0 : vprev + 1;
-      vnext = vprev;
-      vprev = v_kt;
-    }
-  };
-  if (kPingPong && ln.vpart)
-    pingpong(std::true_type{});
-  else if (kPingPong)
-    pingpong(std::false_type{});
-  else if (kSkew && ln.wave >= kWaves / 2)
-    tile_loop(std::true_type{});
-  else
-    tile_loop(std::false_type{});
-
-  if (n_kt_wave == 0) return;
-  if constexpr (SHARED) {
-    // unnormalised state of each column at slot slot0 + chunk of its member's pair
-    const float l = halves_sum(wt.lsum);
-    if (!col_valid) return;
-    const int64_t slot = q_row * a.ws_stride + a.slot0 + it.chunk;
-    float* wo = a.ws_o + slot * D + ln.half * 4;
-#pragma unroll
-    for (int md = 0; md < Gm::MD; ++md)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int r = rr * 4;
-        *reinterpret_cast<float4*>(wo + md * 32 + rr * 8) =
-            make_float4(wt.acc_o[md][r], wt.acc_o[md][r + 1], wt.acc_o[md][r + 2], wt.acc_o[md][r + 3]);
-      }
-    if (ln.half == 0) {
-      a.ws_ml[slot * 2] = wt.m;
-      a.ws_ml[slot * 2 + 1] = l;
-    }
-  } else {
-    wt.store_out(a.out, q_row, ln.half, col_valid);
-  }
-}
-
-template <int D, int HW, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a) {
-  constexpr int QP = 32 * (kCB / HW);
-  // K tile buffers, then V tile buffers (160 KiB for D = 128 with the skew)
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[Geom<D>::LDS_BYTES];
-  const int NHG = a.num_q_heads / HW;
-  Item it{};
-  if constexpr (MODE == kShared) {
-    int id = blockIdx.x;
-    it.hg = id % NHG;
-    id /= NHG;
-    it.tile = id % a.member_tiles;
-    id /= a.member_tiles;
-    it.chunk = id % a.num_chunks;
-    const int gi = id / a.num_chunks;
-    it.member0 = a.group_offsets[gi];
-    it.Lq = a.group_offsets[gi + 1] - it.member0;
-    if (it.tile * QP >= it.Lq) return;
-    it.b = a.group_seqs[it.member0];
-    const int shared = a.shared_lens[it.b];
-    it.key_base = it.chunk * a.chunk_tokens;
-    if (it.key_base >= shared) return;
-    it.Lk = min(shared - it.key_base, a.chunk_tokens);
-  } else {
-    // Workgroups are dispatched to the 8 XCDs round-robin (block B on XCD
-    // B % 8), each XCD with its own L2.  The query tiles of one (sequence, head
-    // group) pair are placed on one XCD at consecutive slots, so the workgroups
-    // that run there together read the same K/V tiles through that L2.
-    const int id = blockIdx.x;
-    const int xcd = id % kXcds;
-    const int slot = id / kXcds;
-    const int pair = (slot / a.tiles_per_pair) * kXcds + xcd;
-    if (pair >= a.num_seqs * NHG) return;
-    const int tile_rev = slot % a.tiles_per_pair;
-    it.hg = pair % NHG;
-    it.b = pair / NHG;
-    it.q0 = a.cu_seqlens_q[it.b];
-    it.Lq = a.cu_seqlens_q[it.b + 1] - it.q0;
-    it.k0 = a.cu_seqlens_k[it.b];
-    it.Lk = a.cu_seqlens_k[it.b + 1] - it.k0;
-    const int n_qt = (it.Lq + QP - 1) / QP;
-    it.tile = n_qt - 1 - tile_rev;  // tiles with the most keys are dispatched first
-    if (it.tile < 0) return;
-  }
-  run_item<D, HW, MODE>(a, lds, it);
-}
-
-// ---------------------------------------------------------------- persistent stream
-
-// The kernel's arguments, read from the kernel argument segment where this is
-// called.  The persistent kernel's scalar registers are too few to hold every
-// argument across its loop, so the ones used once per item are loaded again
-// at each use (the empty asm makes the pointer opaque, so that the loads are
-// neither hoisted out of the loop nor merged).
-__device__ __forceinline__ const PrefillArgs& args_here() {
-  typedef const __attribute__((address_space(4))) PrefillArgs const_args_t;
-  const_args_t* p = (const_args_t*)__builtin_amdgcn_kernarg_segment_ptr();
-  asm volatile("" : "+s"(p));
-  return *(const PrefillArgs*)p;
-}
 
 // record idx of die xcd's list
 __device__ __forceinline__ const_i32_t* item_record(const PrefillArgs& a, int xcd, int idx) {
   return (const_i32_t*)a.plan_items + ((int64_t)xcd * a.items_cap + idx) * kItemInts;
-}
-
-// The part of an item the stream keeps in scalar registers: its key tiles
-// [kt_lo, kt_hi), and for this wave the block's first position and the end of
-// the key tiles it computes; per lane, each column's row of q and out (times
-// Hq, plus the head; -1 past the queries).  Column col's position is
-// min_pos + col (past the sequence's queries the column's output is not
-// written, so its position does not matter).  The rest of the record (piece,
-// split) is read again when the item ends.
-struct Item2 {
-  int kt_lo, kt_hi, min_pos, n_kt_wave;
-  int64_t q_row;
-  __device__ __forceinline__ bool valid() const { return q_row >= 0; }
-};
-
-// Item idx of die xcd's list: what the stream keeps of it, and where its K/V rows are.
-template <int D, int HW>
-__device__ __forceinline__ void load_item(const PrefillArgs& a, int xcd, int idx, int wave, int col, Item2& x,
-                                          TileSource<D>& src) {
-  constexpr int QP = 32 * (kCB / HW);
-  const_i32_t* rec = item_record(a, xcd, idx);
-  const int b = rec[kItB];
-  const int hg = rec[kItHg];
-  const int tile = rec[kItTile];
-  x.kt_lo = rec[kItKtLo];
-  x.kt_hi = rec[kItKtHi];
-  const_i32_t* cq = (const_i32_t*)a.cu_seqlens_q;
-  const_i32_t* ck = (const_i32_t*)a.cu_seqlens_k;
-  const int q0 = cq[b];
-  const int Lq = cq[b + 1] - q0;
-  const int k0 = ck[b];
-  const int Lk = ck[b + 1] - k0;
-  const int Hq = a.num_q_heads;
-  src.init(a, b, (hg * HW) / (Hq / a.num_kv_heads), k0, 0, Lk);
-  const int head = hg * HW + wave % HW;
-  const int first = tile * QP + 32 * (wave / HW);
-  const int qi = first + col;
-  const int shift = Lk - Lq;
-  const bool valid = qi < Lq;
-  x.q_row = valid ? (int64_t)(q0 + qi) * Hq + head : -1;
-  x.min_pos = shift + first;
-  const int w_max_pos = first < Lq ? shift + min(first + 32, Lq) - 1 : -1;
-  x.n_kt_wave = w_max_pos >= 0 ? min(x.kt_hi, w_max_pos / kKT + 1) : x.kt_lo;
 }
 
 // A piece of a split query tile, one wave's columns: write the state (the O^T
@@ -417,6 +145,323 @@ __device__ __forceinline__ void finish_piece(const PrefillArgs& a, int split, in
       *reinterpret_cast<uint2*>(op + md * 32 + rr * 8) = w;
     }
   }
+}
+
+template <int D, int HW, int MODE>
+__device__ __forceinline__ void run_item(const PrefillArgs& a, uint8_t* lds, const Item& it) {
+  using Gm = Geom<D>;
+  constexpr bool SHARED = MODE == kShared;
+  constexpr int QP = 32 * (kCB / HW);  // positions (members) per workgroup
+  Lanes<D> ln;
+  ln.init(a.num_kv_heads);
+  const int Hq = a.num_q_heads;
+  const int G = Hq / a.num_kv_heads;
+  const int g = (it.hg * HW) / G;
+  // Positions are relative to key_base.  Prefill: query i sits at shift + i.
+  // Shared: every column sees the whole chunk, as a query at its last key.
+  const int shift = it.Lk - it.Lq;
+  // this wave's column block: head h, queries (members) first + col
+  const int h = it.hg * HW + ln.wave % HW;
+  const int first = it.tile * QP + 32 * (ln.wave / HW);
+  const int qi = first + ln.col;
+  const bool col_valid = qi < it.Lq;
+  const int pos = (col_valid && !SHARED) ? shift + qi : it.Lk - 1;
+  const int min_pos = SHARED ? it.Lk - 1 : shift + first;
+  const int w_max_pos = first < it.Lq ? (SHARED ? it.Lk - 1 : shift + min(first + 32, it.Lq) - 1) : -1;
+  int64_t q_row;  // row of q[., Hq, D] (times Hq, plus the head)
+  if constexpr (SHARED) {
+    q_row = col_valid ? (int64_t)a.group_seqs[it.member0 + qi] * Hq + h : 0;
+  } else {
+    q_row = (int64_t)(it.q0 + qi) * Hq + h;
+  }
+  const int wg_max_pos = SHARED ? it.Lk - 1 : shift + min(it.tile * QP + QP, it.Lq) - 1;
+  // key tiles [kt0, n_kt) of this item; this wave computes [kt0, n_kt_wave)
+  const int kt0 = it.kt_lo;
+  const int n_kt = it.kt_hi >= 0 ? it.kt_hi : wg_max_pos / kKT + 1;
+  const int n_kt_wave = w_max_pos >= 0 ? min(n_kt, w_max_pos / kKT + 1) : kt0;
+
+  const int lbs = a.log2_block_size;
+  TileSource<D> src;
+  src.init(a, it.b, g, it.k0, it.key_base, it.Lk);
+  int32_t blk[Gm::NBLK];
+#pragma unroll
+  for (int j = 0; j < Gm::NBLK; ++j) blk[j] = 0;
+  WaveTile<D> wt;
+  wt.reset();
+  const float c = a.scale_log2;  // > 0
+
+  // Q^T first: its loads are in flight while the first block ids (scalar
+  // loads) arrive and the first tile's copies are issued
+  wt.load_q(a.q, q_row, col_valid, ln.half);
+  src.fetch(blk, kt0, ln, lbs);
+  src.issue(a, lds, ln, blk, kt0, 0, 0);
+  if (kt0 + 1 < n_kt) src.fetch(blk, kt0 + 1, ln, lbs);
+  wt.settle_q();
+
+  // Pipeline: tile kt+1 is in flight (direct to LDS) while tile kt is
+  // computed; one barrier per tile.  At the barrier of tile kt each wave has
+  // waited for its own copies of tile kt (the only ones in flight) and every
+  // wave has finished its work on the buffers that the copies of tile kt+1
+  // overwrite: K of tile kt-1, and V of tile kt-1 (two buffers) or of tile
+  // kt-2 (three buffers, where the late waves still read V of tile kt-1 after
+  // the barrier).  V buffers of tiles kt - 1, kt and kt + 1 rotate each tile.
+  auto tile_loop = [&](auto LATE) __attribute__((always_inline)) {
+    constexpr bool is_late = decltype(LATE)::value;
+    int vprev = kVBufs - 1, vcur = 0, vnext = 1 % kVBufs;
+    for (int kt = kt0; kt < n_kt; ++kt) {
+      const int kb = (kt - kt0) & 1;  // K buffer of tile kt
+      wait_vmem<0>();
+      __syncthreads();
+      if (kt + 1 < n_kt) src.issue(a, lds, ln, blk, kt + 1, kb ^ 1, vnext);
+      if constexpr (is_late) {
+        if (kt > kt0 && kt <= n_kt_wave) wt.template pv<false>(lds, ln, vprev);
+        if (kt < n_kt_wave) wt.template qk_softmax<false>(lds, ln, kb, kt * kKT, 0, pos, min_pos, c);
+      } else {
+        if (kt < n_kt_wave) {
+          wt.template qk_softmax<true>(lds, ln, kb, kt * kKT, vcur, pos, min_pos, c);
+          wt.template pv<true>(lds, ln, vcur);
+        }
+      }
+      // the next block ids arrive while this wave waits at the next barrier
+      if (kt + 2 < n_kt) src.fetch(blk, kt + 2, ln, lbs);
+      const int v_free = vprev;
+      vprev = vcur;
+      vcur = vnext;
+      vnext = kVBufs == 3 ? v_free : vprev;
+    }
+    // a late wave's last tile (no copies are in flight any more)
+    if constexpr (is_late)
+      if (n_kt_wave == n_kt && n_kt > kt0) wt.template pv<false>(lds, ln, vprev);
+  };
+  // Ping-pong: waves 0-3 (group E, one per SIMD) and 4-7 (group L) alternate
+  // between their products and their softmax, so that in each segment one
+  // wave of a SIMD keeps its matrix core busy while the other computes the
+  // exponentials.  Tile kt:
+  //   segment A: E: O^T += V(kt-1) P(kt-1)^T, S(kt) = K(kt) Q^T;
+  //              L: softmax of S(kt-1), then the copies of K(kt+1)
+  //   segment B: E: softmax of S(kt), then the copies of V(kt+1);
+  //              L: O^T += V(kt-1) P(kt-1)^T, S(kt) = K(kt) Q^T
+  // with one more tile (kt = n_kt) for the last P V product.  K tiles use two
+  // buffers (K(kt+1) goes where K(kt-1) was, whose readers finished before
+  // barrier A of tile kt), V tiles three (V(kt+1) goes where V(kt-2) was).
+  // At barrier A each L wave has waited for its copies of K(kt) and each E
+  // wave for its copies of V(kt-1) (those of V(kt), issued one segment later,
+  // may still be in flight: vector memory operations complete in order).
+  // The two groups run separate copies of the loop (the same barriers in the
+  // same order), so that each keeps only its own values live.
+  auto pingpong = [&](auto GROUP_E) __attribute__((always_inline)) {
+    constexpr bool is_e = decltype(GROUP_E)::value;
+    f32x16_t acc_s[kKB];
+    int vprev = kVBufs - 1, vnext = 1 % kVBufs;  // V buffers of tiles kt-1 and kt+1
+    auto copies = [&](int kt) __attribute__((always_inline)) {
+      if (kt + 1 < n_kt) {
+        src.issue(a, lds, ln, blk, kt + 1, (kt + 1 - kt0) & 1, vnext);
+        if (kt + 2 < n_kt) src.fetch(blk, kt + 2, ln, lbs);
+      }
+    };
+    auto products = [&](int kt) __attribute__((always_inline)) {
+      if (kt > kt0 && kt - 1 < n_kt_wave) wt.template pv<false>(lds, ln, vprev);
+      if (kt < n_kt_wave) wt.template qk<false>(lds, ln, (kt - kt0) & 1, 0, acc_s);
+    };
+    for (int kt = kt0; kt <= n_kt; ++kt) {
+      if (is_e && kt > kt0 && kt < n_kt)
+        wait_vmem<Gm::IPW>();
+      else
+        wait_vmem<0>();
+      __syncthreads();
+      if constexpr (is_e) {
+        products(kt);
+      } else {
+        if (kt > kt0 && kt - 1 < n_kt_wave) wt.softmax(ln, acc_s, (kt - 1) * kKT, pos, min_pos, c);
+        copies(kt);
+      }
+      __syncthreads();
+      if constexpr (is_e) {
+        if (kt < n_kt_wave) wt.softmax(ln, acc_s, kt * kKT, pos, min_pos, c);
+        copies(kt);
+      } else {
+        products(kt);
+      }
+      // V buffers: tile kt's becomes the previous one, tile kt+2's takes the
+      // oldest (that of tile kt-1)
+      const int v_kt = vprev == kVBufs - 1 ? 0 : vprev + 1;
+      vnext = vprev;
+      vprev = v_kt;
+    }
+  };
+  if (kPingPong && ln.vpart)
+    pingpong(std::true_type{});
+  else if (kPingPong)
+    pingpong(std::false_type{});
+  else if (kSkew && ln.wave >= kWaves / 2)
+    tile_loop(std::true_type{});
+  else
+    tile_loop(std::false_type{});
+
+  if (n_kt_wave <= kt0) return;
+  if constexpr (SHARED) {
+    // unnormalised state of each column at slot slot0 + chunk of its member's pair
+    const float l = halves_sum(wt.lsum);
+    if (!col_valid) return;
+    const int64_t slot = q_row * a.ws_stride + a.slot0 + it.chunk;
+    float* wo = a.ws_o + slot * D + ln.half * 4;
+#pragma unroll
+    for (int md = 0; md < Gm::MD; ++md)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int r = rr * 4;
+        *reinterpret_cast<float4*>(wo + md * 32 + rr * 8) =
+            make_float4(wt.acc_o[md][r], wt.acc_o[md][r + 1], wt.acc_o[md][r + 2], wt.acc_o[md][r + 3]);
+      }
+    if (ln.half == 0) {
+      a.ws_ml[slot * 2] = wt.m;
+      a.ws_ml[slot * 2 + 1] = l;
+    }
+  } else if (it.split < 0) {
+    wt.store_out(a.out, q_row, ln.half, col_valid);
+  } else {
+    finish_piece<D>(a, it.split, it.slot, it.pc & 0xffff, it.pc >> 16, col_valid ? q_row : -1, wt, ln.wave, ln.lane);
+  }
+}
+
+template <int D, int HW, int MODE>
+__global__ __launch_bounds__(kThreads, 1) void prefill_mfma_kernel(PrefillArgs a) {
+  constexpr int QP = 32 * (kCB / HW);
+  // K tile buffers, then V tile buffers (160 KiB for D = 128 with the skew)
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[Geom<D>::LDS_BYTES];
+  const int NHG = a.num_q_heads / HW;
+  Item it{};
+  if constexpr (MODE == kShared) {
+    int id = blockIdx.x;
+    it.hg = id % NHG;
+    id /= NHG;
+    it.tile = id % a.member_tiles;
+    id /= a.member_tiles;
+    it.chunk = id % a.num_chunks;
+    const int gi = id / a.num_chunks;
+    it.member0 = a.group_offsets[gi];
+    it.Lq = a.group_offsets[gi + 1] - it.member0;
+    if (it.tile * QP >= it.Lq) return;
+    it.b = a.group_seqs[it.member0];
+    const int shared = a.shared_lens[it.b];
+    it.key_base = it.chunk * a.chunk_tokens;
+    if (it.key_base >= shared) return;
+    it.Lk = min(shared - it.key_base, a.chunk_tokens);
+  } else {
+    // Workgroups are dispatched to the 8 XCDs round-robin (block B on XCD
+    // B % 8), each XCD with its own L2.  The query tiles of one (sequence, head
+    // group) pair are placed on one XCD at consecutive slots, so the workgroups
+    // that run there together read the same K/V tiles through that L2.
+    const int id = blockIdx.x;
+    const int xcd = id % kXcds;
+    const int slot = id / kXcds;
+    const int pair = (slot / a.tiles_per_pair) * kXcds + xcd;
+    if (pair >= a.num_seqs * NHG) return;
+    const int tile_rev = slot % a.tiles_per_pair;
+    it.hg = pair % NHG;
+    it.b = pair / NHG;
+    it.q0 = a.cu_seqlens_q[it.b];
+    it.Lq = a.cu_seqlens_q[it.b + 1] - it.q0;
+    it.k0 = a.cu_seqlens_k[it.b];
+    it.Lk = a.cu_seqlens_k[it.b + 1] - it.k0;
+    const int n_qt = (it.Lq + QP - 1) / QP;
+    it.tile = n_qt - 1 - tile_rev;  // tiles with the most keys are dispatched first
+    if (it.tile < 0) return;
+  }
+  run_item<D, HW, MODE>(a, lds, it);
+}
+
+// ---------------------------------------------------------------- planned grid
+
+// One workgroup per item of the plan's lists (workgroup w takes item w / 8 of
+// die w % 8's list; the dispatcher places it on that die): the query tiles
+// with their long key ranges cut into pieces, the largest pairs first, so
+// that the dispatcher's own order balances the dies' workgroups.  Pieces of a
+// split query tile are merged by the last to arrive, as in the persistent
+// kernel.
+template <int D, int HW>
+__global__ __launch_bounds__(kThreads, 1) void prefill_items_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[Geom<D>::LDS_BYTES];
+  const int xcd = blockIdx.x % kPlanXcds;
+  const int idx = blockIdx.x / kPlanXcds;
+  const_i32_t* hdr = (const_i32_t*)a.plan_hdr;
+  // a plan that overflowed its lists left holes in them (the host sizes the
+  // lists so that this cannot happen)
+  if (idx >= min(hdr[kPlanXcds + xcd], a.items_cap) || hdr[kHdrOverflow] != 0) return;
+  const_i32_t* rec = item_record(a, xcd, idx);
+  Item it{};
+  it.b = rec[kItB];
+  it.hg = rec[kItHg];
+  it.tile = rec[kItTile];
+  it.kt_lo = rec[kItKtLo];
+  it.kt_hi = rec[kItKtHi];
+  it.pc = rec[kItChunk];
+  it.split = rec[kItSplit];
+  it.slot = rec[kItSlot];
+  const_i32_t* cq = (const_i32_t*)a.cu_seqlens_q;
+  const_i32_t* ck = (const_i32_t*)a.cu_seqlens_k;
+  it.q0 = cq[it.b];
+  it.Lq = cq[it.b + 1] - it.q0;
+  it.k0 = ck[it.b];
+  it.Lk = ck[it.b + 1] - it.k0;
+  run_item<D, HW, kGrid>(a, lds, it);
+}
+
+// ---------------------------------------------------------------- persistent stream
+
+// The kernel's arguments, read from the kernel argument segment where this is
+// called.  The persistent kernel's scalar registers are too few to hold every
+// argument across its loop, so the ones used once per item are loaded again
+// at each use (the empty asm makes the pointer opaque, so that the loads are
+// neither hoisted out of the loop nor merged).
+__device__ __forceinline__ const PrefillArgs& args_here() {
+  typedef const __attribute__((address_space(4))) PrefillArgs const_args_t;
+  const_args_t* p = (const_args_t*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(p));
+  return *(const PrefillArgs*)p;
+}
+
+// The part of an item the stream keeps in scalar registers: its key tiles
+// [kt_lo, kt_hi), and for this wave the block's first position and the end of
+// the key tiles it computes; per lane, each column's row of q and out (times
+// Hq, plus the head; -1 past the queries).  Column col's position is
+// min_pos + col (past the sequence's queries the column's output is not
+// written, so its position does not matter).  The rest of the record (piece,
+// split) is read again when the item ends.
+struct Item2 {
+  int kt_lo, kt_hi, min_pos, n_kt_wave;
+  int64_t q_row;
+  __device__ __forceinline__ bool valid() const { return q_row >= 0; }
+};
+
+// Item idx of die xcd's list: what the stream keeps of it, and where its K/V rows are.
+template <int D, int HW>
+__device__ __forceinline__ void load_item(const PrefillArgs& a, int xcd, int idx, int wave, int col, Item2& x,
+                                          TileSource<D>& src) {
+  constexpr int QP = 32 * (kCB / HW);
+  const_i32_t* rec = item_record(a, xcd, idx);
+  const int b = rec[kItB];
+  const int hg = rec[kItHg];
+  const int tile = rec[kItTile];
+  x.kt_lo = rec[kItKtLo];
+  x.kt_hi = rec[kItKtHi];
+  const_i32_t* cq = (const_i32_t*)a.cu_seqlens_q;
+  const_i32_t* ck = (const_i32_t*)a.cu_seqlens_k;
+  const int q0 = cq[b];
+  const int Lq = cq[b + 1] - q0;
+  const int k0 = ck[b];
+  const int Lk = ck[b + 1] - k0;
+  const int Hq = a.num_q_heads;
+  src.init(a, b, (hg * HW) / (Hq / a.num_kv_heads), k0, 0, Lk);
+  const int head = hg * HW + wave % HW;
+  const int first = tile * QP + 32 * (wave / HW);
+  const int qi = first + col;
+  const int shift = Lk - Lq;
+  const bool valid = qi < Lq;
+  x.q_row = valid ? (int64_t)(q0 + qi) * Hq + head : -1;
+  x.min_pos = shift + first;
+  const int w_max_pos = first < Lq ? shift + min(first + 32, Lq) - 1 : -1;
+  x.n_kt_wave = w_max_pos >= 0 ? min(x.kt_hi, w_max_pos / kKT + 1) : x.kt_lo;
 }
 
 // The end of item idx for one wave: its output (if the wave computed any of
@@ -664,6 +709,22 @@ hipError_t launch(const PrefillArgs& a, int32_t head_dim, int64_t blocks, int HW
   return hipErrorInvalidValue;
 }
 
+hipError_t launch_items(const PrefillArgs& a, int32_t head_dim, int HW, hipStream_t stream) {
+  const int64_t blocks = (int64_t)kPlanXcds * a.items_cap;
+#define PKV_ITEMS_CASE(DD, HH) \
+  if (head_dim == DD && HW == HH) return launch_kernel(prefill_items_kernel<DD, HH>, blocks, a, stream);
+  PKV_ITEMS_CASE(128, 8)
+  PKV_ITEMS_CASE(128, 4)
+  PKV_ITEMS_CASE(128, 2)
+  PKV_ITEMS_CASE(128, 1)
+  PKV_ITEMS_CASE(64, 8)
+  PKV_ITEMS_CASE(64, 4)
+  PKV_ITEMS_CASE(64, 2)
+  PKV_ITEMS_CASE(64, 1)
+#undef PKV_ITEMS_CASE
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_stream(const PrefillArgs& a, int32_t head_dim, int HW, hipStream_t stream) {
 #define PKV_STREAM_CASE(DD, HH) \
   if (head_dim == DD && HW == HH) return launch_kernel(prefill_stream_kernel<DD, HH>, kPersistWgs, a, stream);
@@ -683,7 +744,7 @@ hipError_t launch_stream(const PrefillArgs& a, int32_t head_dim, int HW, hipStre
 
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int32_t head_dim, hipStream_t stream) {
   const int HW = heads_per_wg(a.num_q_heads, a.num_kv_heads);
-  if (a.plan_hdr) return launch_stream(a, head_dim, HW, stream);
+  if (a.plan_hdr) return kPlanPersistent ? launch_stream(a, head_dim, HW, stream) : launch_items(a, head_dim, HW, stream);
   const int QP = 32 * (kCB / HW);
   PrefillArgs b = a;
   b.tiles_per_pair = (a.max_seqlen_q + QP - 1) / QP;

@@ -62,6 +62,13 @@ constexpr bool kSkew = PKV_PREFILL_SKEW != 0;
 #endif
 constexpr bool kPingPong = PKV_PREFILL_PINGPONG != 0;
 static_assert(!kPingPong || kSkew, "the ping-pong schedule keeps three V tile buffers");
+// With a workspace (a device-side plan of the work): one persistent workgroup
+// per CU walking its die's list as one stream of tiles (1), or one workgroup
+// per item of the lists, dispatched in list order (0).
+#ifndef PKV_PREFILL_PERSISTENT
+#define PKV_PREFILL_PERSISTENT 0
+#endif
+constexpr bool kPlanPersistent = PKV_PREFILL_PERSISTENT != 0;
 // Compile-time tuning knobs (defaults are the measured choice): LDS fragment
 // reads in flight ahead of the MFMAs (K, V^T), and the wave priority taken
 // while a wave issues its matrix products (0: never raised).
