@@ -342,13 +342,14 @@ int64_t pkv_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32
  * vector units in fp32 and ignores the workspace.
  *
  * With a workspace (bf16), a planning kernel reads cu_seqlens on the device
- * and writes per-die work lists into it, and a persistent kernel (one
- * workgroup per compute unit) works through them: sequences with the most
- * keys first, long query tiles cut along their keys into pieces whose
- * partial softmax states are merged (in piece order, so results are
- * deterministic).  Without one, each query tile is a workgroup of a single
- * launch.  Both compute the same function within rounding; the split and
- * merge change the rounding order, not the result's definition.
+ * and writes per-die work lists into it (sequences with the most keys first,
+ * long query tiles cut along their keys into pieces whose partial softmax
+ * states are merged in piece order, so results are deterministic), and one
+ * workgroup per listed item works through them (the library can also be
+ * built to walk the lists with one persistent workgroup per compute unit).
+ * Without one, each query tile is a workgroup of a single launch.  Both
+ * compute the same function within rounding; the split and merge change the
+ * rounding order, not the result's definition.
  */
 int64_t pkv_prefill_workspace_bytes(int32_t num_seqs, int32_t max_seqlen_q, int32_t num_q_heads,
                                     int32_t num_kv_heads, int32_t head_dim, int32_t dtype);

@@ -415,9 +415,10 @@ def paged_prefill_attn(q, k, v, cu_seqlens_q, cu_seqlens_k, block_tables, out, m
                        max_seqlen_k=None, scale=None, workspace=None, persistent=None):
     """Causal varlen prefill: q [sum Lq, Hq, D]; k, v the caches (block_tables given) or packed [sum Lk, Hkv, D].
 
-    bf16: ``persistent=True`` runs the persistent kernel over device-planned work lists in
-    ``workspace`` (allocated here when None); otherwise the one-launch kernel.  The default
-    (None) is persistent exactly when a workspace is passed."""
+    bf16: ``persistent=True`` runs over device-planned work lists in ``workspace`` (allocated
+    here when None): long query tiles cut into key pieces, one workgroup per planned item;
+    otherwise the one-launch kernel.  The default (None) plans exactly when a workspace is
+    passed."""
     torch = _torch()
     _dev(q, "q", ndim=3)
     _dev(out, "out", q.dtype, 3)
