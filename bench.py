@@ -370,7 +370,7 @@ def main():
     ap.add_argument("--overlap-prefill", action="store_true",
                     help="run prefill on a second stream concurrently with decode (after kv_store); the decode "
                          "kernel then shares the GPU, so its event time is not the kernel's own")
-    ap.add_argument("--prefill-persistent", action="store_true",
+    ap.add_argument("--prefill-planned", action="store_true",
                     help="prefill through a workspace: the device-side plan (query tiles with long key ranges cut "
                          "into pieces) run as one workgroup per planned item, instead of the one-launch kernel")
     ap.add_argument("--graph", action="store_true",
@@ -443,7 +443,7 @@ def main():
         pq, pbt, cuq, cuk = dev(w.pre_q, bf), dev(w.pre_block_tables), dev(w.cu_seqlens_q), dev(w.cu_seqlens_k)
         pout = torch.empty_like(pq)
         pws = None
-        if args.prefill_persistent:
+        if args.prefill_planned:
             need = pkv.prefill_workspace_bytes(int(len(w.cu_seqlens_q) - 1), w.max_seqlen_q, w.num_q_heads,
                                                w.num_kv_heads, w.head_dim, 1 if bf else 0)
             pws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
@@ -451,7 +451,7 @@ def main():
         def prefill():
             pkv.paged_prefill_attn(pq, kc, vc, cuq, cuk, pbt, pout, max_seqlen_q=w.max_seqlen_q,
                                    max_seqlen_k=w.max_seqlen_k, scale=w.scale, workspace=pws,
-                                   persistent=args.prefill_persistent)
+                                   planned=args.prefill_planned)
     torch.cuda.synchronize()
     log("inputs resident on the GPU")
 
@@ -617,7 +617,7 @@ def main():
             "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
             "block_size": w.block_size, "num_blocks": w.num_blocks,
             "value_definition": "decode algorithmic K/V bytes (logical, each sequence's context read once per KV "
-                                "head) per whole-step wall time" if has_dec else "prefill flops per step time",
+                                "head) per step time (HIP events from the step's first kernel to its last)" if has_dec else "prefill flops per step time",
             "decode_kv_gb": round(kv_bytes / 1e9, 4),
             "parallelism": "single-gpu",
             "prefill_overlapped_with_decode": bool(overlap),

@@ -412,10 +412,10 @@ def prefill_workspace_bytes(num_seqs, max_seqlen_q, num_q_heads, num_kv_heads, h
 
 
 def paged_prefill_attn(q, k, v, cu_seqlens_q, cu_seqlens_k, block_tables, out, max_seqlen_q=None,
-                       max_seqlen_k=None, scale=None, workspace=None, persistent=None):
+                       max_seqlen_k=None, scale=None, workspace=None, planned=None):
     """Causal varlen prefill: q [sum Lq, Hq, D]; k, v the caches (block_tables given) or packed [sum Lk, Hkv, D].
 
-    bf16: ``persistent=True`` runs over device-planned work lists in ``workspace`` (allocated
+    bf16: ``planned=True`` runs over device-planned work lists in ``workspace`` (allocated
     here when None): long query tiles cut into key pieces, one workgroup per planned item;
     otherwise the one-launch kernel.  The default (None) plans exactly when a workspace is
     passed."""
@@ -450,9 +450,9 @@ def paged_prefill_attn(q, k, v, cu_seqlens_q, cu_seqlens_k, block_tables, out, m
         max_seqlen_k = int((ck[1:] - ck[:-1]).max()) if B else 0
     sc = 0.0 if scale is None else float(scale)
     code = _dtype_code(q)
-    if persistent is None:
-        persistent = workspace is not None
-    if not persistent:
+    if planned is None:
+        planned = workspace is not None
+    if not planned:
         workspace = None
     elif workspace is None:
         need = prefill_workspace_bytes(B, int(max_seqlen_q), Hq, Hkv, D, code)

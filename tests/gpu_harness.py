@@ -83,17 +83,17 @@ class DeviceStep:
         pkv.paged_decode_attn(self.dec_q, self.k_cache, self.v_cache, self.dec_bt, self.dec_cl, w.scale, self.dec_out,
                               max_context_len=w.max_context_len, split_tokens=split_tokens)
 
-    def prefill(self, persistent: bool = True):
-        """persistent: the planned persistent kernel (the binding allocates its workspace)."""
+    def prefill(self, planned: bool = True):
+        """planned: the device-planned work lists (the binding allocates their workspace)."""
         w = self.w
         pkv.paged_prefill_attn(self.pre_q, self.k_cache, self.v_cache, self.cu_q, self.cu_k, self.pre_bt,
                                self.pre_out, max_seqlen_q=w.max_seqlen_q, max_seqlen_k=w.max_seqlen_k, scale=w.scale,
-                               persistent=persistent)
+                               planned=planned)
 
-    def step(self, split_tokens: int = 0, persistent: bool = True):
+    def step(self, split_tokens: int = 0, planned: bool = True):
         self.store()
         if self.pre:
-            self.prefill(persistent)
+            self.prefill(planned)
         if self.dec:
             self.decode(split_tokens)
         torch.cuda.synchronize()

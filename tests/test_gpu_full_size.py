@@ -76,7 +76,7 @@ def _one_launch_prefill(r):
     s, w = r.step, r.w
     out = torch.empty_like(s.pre_out)
     pkv.paged_prefill_attn(s.pre_q, s.k_cache, s.v_cache, s.cu_q, s.cu_k, s.pre_bt, out, max_seqlen_q=w.max_seqlen_q,
-                           max_seqlen_k=w.max_seqlen_k, scale=w.scale, persistent=False)
+                           max_seqlen_k=w.max_seqlen_k, scale=w.scale, planned=False)
     torch.cuda.synchronize()
     return out
 
@@ -118,7 +118,7 @@ def test_prefix_cached_prefill_every_row(c4):
 
 
 def test_prefix_cached_prefill_one_launch_kernel_same_bits(c4):
-    """No query tile here has more key tiles than the piece cap, so the persistent
+    """No query tile here has more key tiles than the piece cap, so the planned
     kernel computes every tile exactly as the one-launch kernel does."""
     out = _one_launch_prefill(c4)
     assert torch.equal(out.view(torch.int16), c4.step.pre_out.view(torch.int16))
@@ -130,7 +130,7 @@ def test_prefix_cached_prefill_shared_equals_private_bitwise(c4):
     k2, v2, t2 = _with_private_copies(s, w.pre_block_tables, rows, w.shared_blocks)
     out2 = torch.empty_like(s.pre_out)
     pkv.paged_prefill_attn(s.pre_q, k2, v2, s.cu_q, s.cu_k, to_dev(t2), out2, max_seqlen_q=w.max_seqlen_q,
-                           max_seqlen_k=w.max_seqlen_k, scale=w.scale, persistent=True)
+                           max_seqlen_k=w.max_seqlen_k, scale=w.scale, planned=True)
     torch.cuda.synchronize()
     assert torch.equal(out2.view(torch.int16), s.pre_out.view(torch.int16))
 
@@ -164,7 +164,7 @@ def test_mixed_step_prefill_every_row(c5):
 
 
 def test_mixed_step_prefill_one_launch_kernel_every_row(c5):
-    """The chunks' query tiles are cut into pieces by the persistent kernel; the
+    """The chunks' query tiles are cut into pieces by the planned path; the
     one-launch kernel computes them whole.  Both against the oracle."""
     w = c5.w
     got = to_host(_one_launch_prefill(c5), w.dtype)

@@ -86,16 +86,16 @@ PREFILL_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("persistent", [True, False], ids=["persistent", "one-launch"])
+@pytest.mark.parametrize("planned", [True, False], ids=["planned", "one-launch"])
 @pytest.mark.parametrize("shape", PREFILL_SHAPES, ids=lambda s: "-".join(map(str, s)))
-def test_prefill_tiny_sweep(shape, persistent):
-    """With the persistent kernel the pairs (3, 1500) and (64, 1100) are cut into
+def test_prefill_tiny_sweep(shape, planned):
+    """With the planned work lists the pairs (3, 1500) and (64, 1100) are cut into
     pieces of 4 key tiles (the smallest cap), so the piece merge is covered."""
     dtype, hq, hkv, d, bs = shape
     w = _prefill_case(dtype, hq, hkv, d, bs, PREFILL_PAIRS, seed=hq * 3 + bs)
-    log(f"prefill sweep {shape} persistent={persistent}")
+    log(f"prefill sweep {shape} planned={planned}")
     step = DeviceStep(w)
-    step.step(persistent=persistent)
+    step.step(planned=planned)
     kc, vc = _check_store(step, w)
     ref = oracle.prefill(w.pre_q, kc, vc, w.cu_seqlens_q, w.cu_seqlens_k, w.pre_block_tables, w.scale, dtype,
                          w.block_size)
@@ -103,7 +103,7 @@ def test_prefill_tiny_sweep(shape, persistent):
     assert err <= tol(dtype), f"max abs error {err}"
 
 
-def test_prefill_persistent_repeats_bitwise_and_rejects_small_workspace():
+def test_prefill_planned_repeats_bitwise_and_rejects_small_workspace():
     """The last piece to arrive merges all pieces in piece order, so repeated
     calls give the same bits whichever piece finishes last."""
     w = _prefill_case("bf16", 32, 8, 128, 16, [(3, 1500), (64, 1100), (200, 700), (700, 3000)], seed=21)
