@@ -145,8 +145,9 @@ int pkv_rope_kv_store(void* q, const void* k, const void* v, const int32_t* posi
  * the context lengths are mixed.
  *
  * pkv_decode_split_tokens returns the split the library picks for a shape (a
- * multiple of 64, or PKV_SPLIT_BALANCED); pass it, or 0 for the same choice,
- * or any positive multiple of 64, or PKV_SPLIT_BALANCED.
+ * multiple of 64, or PKV_SPLIT_BALANCED where even the longest contexts would
+ * give the fixed split at most about 1024 waves, one per SIMD); pass it, or 0
+ * for the same choice, or any positive multiple of 64, or PKV_SPLIT_BALANCED.
  * pkv_decode_workspace_bytes gives the workspace size that split needs (0
  * when no sequence can span two splits).
  */

@@ -100,12 +100,16 @@ int64_t balanced_state_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head
   return (int64_t)balance_pieces(num_seqs) * num_q_heads * (head_dim + 2) * (int64_t)sizeof(float) +
          (int64_t)num_seqs * 2 * (int64_t)sizeof(int32_t);
 }
-// the library's choice for split_tokens = 0
+// The library's choice for split_tokens = 0: equal pieces where even the
+// longest contexts would give the fixed split's grid at most kBalancePieces
+// waves (about one per SIMD), so that the waves of such a small grid finish
+// together; the fixed split otherwise, and one split per sequence for
+// contexts of at most 256 tokens.
 bool auto_balanced(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
-  (void)num_seqs;
-  (void)num_kv_heads;
-  (void)max_context_len;
-  return false;
+  if (num_seqs < 1 || num_kv_heads < 1 || max_context_len <= 256) return false;
+  const int32_t split = auto_split(num_seqs, num_kv_heads, max_context_len);
+  const int64_t waves = (int64_t)num_seqs * std::max(1, num_kv_heads / 8) * ((max_context_len + split - 1) / split);
+  return waves <= kBalancePieces;
 }
 
 struct DecodeCall {
