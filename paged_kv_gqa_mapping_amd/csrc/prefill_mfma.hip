@@ -195,7 +195,15 @@ __device__ __forceinline__ void run_item(const PrefillArgs& a, uint8_t* lds, con
   wt.load_q(a.q, q_row, col_valid, ln.half);
   src.fetch(blk, kt0, ln, lbs);
   src.issue(a, lds, ln, blk, kt0, 0, 0);
-  if (kt0 + 1 < n_kt) src.fetch(blk, kt0 + 1, ln, lbs);
+  // block ids of the next tile: vector-loaded for the one-barrier loop
+  // (taken out after the next barrier), scalar-loaded for the ping-pong loop
+  int32_t vblk = 0;
+  if (kt0 + 1 < n_kt) {
+    if (!kPingPong)
+      vblk = src.fetch_v(kt0 + 1, ln);
+    else
+      src.fetch(blk, kt0 + 1, ln, lbs);
+  }
   wt.settle_q();
 
   // Pipeline: tile kt+1 is in flight (direct to LDS) while tile kt is
@@ -212,7 +220,13 @@ __device__ __forceinline__ void run_item(const PrefillArgs& a, uint8_t* lds, con
       const int kb = (kt - kt0) & 1;  // K buffer of tile kt
       wait_vmem<0>();
       __syncthreads();
-      if (kt + 1 < n_kt) src.issue(a, lds, ln, blk, kt + 1, kb ^ 1, vnext);
+      if (kt + 1 < n_kt) {
+        // tile kt+1's block ids arrived with this barrier's wait; tile kt+2's
+        // are requested before its copies (the next barrier's wait covers them)
+        TileSource<D>::take(blk, vblk);
+        if (kt + 2 < n_kt) vblk = src.fetch_v(kt + 2, ln);
+        src.issue(a, lds, ln, blk, kt + 1, kb ^ 1, vnext);
+      }
       if constexpr (is_late) {
         if (kt > kt0 && kt <= n_kt_wave) wt.template pv<false>(lds, ln, vprev);
         if (kt < n_kt_wave) wt.template qk_softmax<false>(lds, ln, kb, kt * kKT, 0, pos, min_pos, c);
@@ -222,8 +236,6 @@ __device__ __forceinline__ void run_item(const PrefillArgs& a, uint8_t* lds, con
           wt.template pv<true>(lds, ln, vcur);
         }
       }
-      // the next block ids arrive while this wave waits at the next barrier
-      if (kt + 2 < n_kt) src.fetch(blk, kt + 2, ln, lbs);
       const int v_free = vprev;
       vprev = vcur;
       vcur = vnext;

@@ -240,11 +240,12 @@ template <int D>
 struct TileSource {
   using Gm = Geom<D>;
   const_i32_t* table;
-  int k0, key_base, last_key;
+  int k0, key_base, last_key, lbs_;
   uint32_t head_bytes;
 
   __device__ __forceinline__ void init(const PrefillArgs& a, int b, int g, int k0_, int key_base_, int Lk) {
     table = a.block_tables ? (const_i32_t*)(a.block_tables + (int64_t)b * a.max_blocks_per_seq) : nullptr;
+    lbs_ = a.log2_block_size;
     k0 = k0_;
     key_base = key_base_;
     last_key = Lk - 1;
@@ -258,6 +259,21 @@ struct TileSource {
 #pragma unroll
     for (int j = 0; j < Gm::NBLK; ++j)
       blk[j] = table[uniform((key_base + min(t * kKT + Gm::RW * ln.rgroup + 8 * j, last_key)) >> lbs)];
+  }
+
+  // The same block ids, fetched with a vector load into lanes 0 .. NBLK - 1
+  // (taken out with take()): vector loads wait on the vector memory counter,
+  // while scalar loads share a counter with the LDS reads, so that any
+  // fragment read issued after a scalar fetch would wait for it.
+  __device__ __forceinline__ int32_t fetch_v(int t, const Lanes<D>& ln) const {
+    if (!table) return 0;
+    const int j = ln.lane < Gm::NBLK ? ln.lane : 0;
+    const int row = key_base + min(t * kKT + Gm::RW * ln.rgroup + 8 * j, last_key);
+    return ((const int32_t*)table)[row >> lbs_];
+  }
+  __device__ __forceinline__ static void take(int32_t (&blk)[Gm::NBLK], int32_t v) {
+#pragma unroll
+    for (int j = 0; j < Gm::NBLK; ++j) blk[j] = __builtin_amdgcn_readlane(v, j);
   }
 
   // LDS byte address of this wave's rows in K buffer kb or V buffer vb (its part)
