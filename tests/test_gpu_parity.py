@@ -122,6 +122,24 @@ def test_prefill_planned_repeats_bitwise_and_rejects_small_workspace():
                                scale=w.scale, workspace=small)
 
 
+@pytest.mark.parametrize("planned", [True, False], ids=["planned", "one-launch"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_prefill_sequences_without_new_queries(dtype, planned):
+    """Sequences of a batch may bring no new queries (an empty chunk, Lq = 0,
+    between others): they launch no work, and their neighbours' rows, keys
+    and stored tokens are unaffected."""
+    pairs = [(0, 40), (5, 5), (0, 300), (40, 300), (0, 1), (129, 1000)]
+    w = _prefill_case(dtype, 32, 8, 128, 16, pairs, seed=23)
+    log(f"prefill with empty chunks {dtype} planned={planned}")
+    step = DeviceStep(w)
+    step.step(planned=planned)
+    kc, vc = _check_store(step, w)
+    ref = oracle.prefill(w.pre_q, kc, vc, w.cu_seqlens_q, w.cu_seqlens_k, w.pre_block_tables, w.scale, dtype,
+                         w.block_size)
+    err = max_abs(to_host(step.pre_out, dtype), ref, dtype)
+    assert err <= tol(dtype), f"max abs error {err}"
+
+
 # packed k/v (no block table): group sizes 1-8, both head dims; the last pair walks 12 key tiles
 PACKED_SHAPES = [("bf16", 16, 4, 128), ("f32", 16, 4, 128), ("bf16", 64, 8, 128), ("bf16", 8, 8, 64),
                  ("bf16", 16, 8, 64), ("f32", 8, 2, 64)]
