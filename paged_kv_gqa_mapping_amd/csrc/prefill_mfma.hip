@@ -168,12 +168,14 @@ __device__ __forceinline__ void run_item(const PrefillArgs& a, uint8_t* lds, con
   const int pos = (col_valid && !SHARED) ? shift + qi : it.Lk - 1;
   const int min_pos = SHARED ? it.Lk - 1 : shift + first;
   const int w_max_pos = first < it.Lq ? (SHARED ? it.Lk - 1 : shift + min(first + 32, it.Lq) - 1) : -1;
-  int64_t q_row;  // row of q[., Hq, D] (times Hq, plus the head)
-  if constexpr (SHARED) {
-    q_row = col_valid ? (int64_t)a.group_seqs[it.member0 + qi] * Hq + h : 0;
-  } else {
-    q_row = (int64_t)(it.q0 + qi) * Hq + h;
-  }
+  // row of q[., Hq, D] (times Hq, plus the head) of query (member) q of this
+  // wave's head; computed again after the tile loop rather than kept live
+  auto row_of = [&](int q) -> int64_t {
+    if constexpr (SHARED)
+      return q < it.Lq ? (int64_t)a.group_seqs[it.member0 + q] * Hq + h : 0;
+    else
+      return (int64_t)(it.q0 + q) * Hq + h;
+  };
   const int wg_max_pos = SHARED ? it.Lk - 1 : shift + min(it.tile * QP + QP, it.Lq) - 1;
   // key tiles [kt0, n_kt) of this item; this wave computes [kt0, n_kt_wave)
   const int kt0 = it.kt_lo;
@@ -192,7 +194,7 @@ __device__ __forceinline__ void run_item(const PrefillArgs& a, uint8_t* lds, con
 
   // Q^T first: its loads are in flight while the first block ids (scalar
   // loads) arrive and the first tile's copies are issued
-  wt.load_q(a.q, q_row, col_valid, ln.half);
+  wt.load_q(a.q, row_of(qi), col_valid, ln.half);
   src.fetch(blk, kt0, ln, lbs);
   src.issue(a, lds, ln, blk, kt0, 0, 0);
   // block ids of the next tile: vector-loaded for the one-barrier loop
@@ -225,14 +227,21 @@ __device__ __forceinline__ void run_item(const PrefillArgs& a, uint8_t* lds, con
         // are requested before its copies (the next barrier's wait covers them)
         TileSource<D>::take(blk, vblk);
         if (kt + 2 < n_kt) vblk = src.fetch_v(kt + 2, ln);
-        src.issue(a, lds, ln, blk, kt + 1, kb ^ 1, vnext);
+        // the late waves copy K rows, which the next tile needs first: at once
+        if constexpr (is_late) src.issue(a, lds, ln, blk, kt + 1, kb ^ 1, vnext);
       }
       if constexpr (is_late) {
         if (kt > kt0 && kt <= n_kt_wave) wt.template pv<false>(lds, ln, vprev);
         if (kt < n_kt_wave) wt.template qk_softmax<false>(lds, ln, kb, kt * kKT, 0, pos, min_pos, c);
       } else {
+        // the early waves copy V rows, needed only by the next tile's P V:
+        // after their Q K^T, so that the tile starts with matrix products
+        // while the late waves' copies pass the address path
+        f32x16_t acc_s[kKB];
+        if (kt < n_kt_wave) wt.template qk<true>(lds, ln, kb, vcur, acc_s);
+        if (kt + 1 < n_kt) src.issue(a, lds, ln, blk, kt + 1, kb ^ 1, vnext);
         if (kt < n_kt_wave) {
-          wt.template qk_softmax<true>(lds, ln, kb, kt * kKT, vcur, pos, min_pos, c);
+          wt.softmax(ln, acc_s, kt * kKT, pos, min_pos, c);
           wt.template pv<true>(lds, ln, vcur);
         }
       }
@@ -311,12 +320,19 @@ __device__ __forceinline__ void run_item(const PrefillArgs& a, uint8_t* lds, con
     tile_loop(std::false_type{});
 
   if (n_kt_wave <= kt0) return;
+  // this lane's column from the lane id (two instructions) instead of a
+  // register held through the loop
+  const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int half_e = lane_e >> 5;
+  const int qi_e = first + (lane_e & 31);
+  const int64_t q_row = row_of(qi_e);
+  const bool col_valid_e = qi_e < it.Lq;
   if constexpr (SHARED) {
     // unnormalised state of each column at slot slot0 + chunk of its member's pair
     const float l = halves_sum(wt.lsum);
-    if (!col_valid) return;
+    if (!col_valid_e) return;
     const int64_t slot = q_row * a.ws_stride + a.slot0 + it.chunk;
-    float* wo = a.ws_o + slot * D + ln.half * 4;
+    float* wo = a.ws_o + slot * D + half_e * 4;
 #pragma unroll
     for (int md = 0; md < Gm::MD; ++md)
 #pragma unroll
@@ -325,14 +341,15 @@ __device__ __forceinline__ void run_item(const PrefillArgs& a, uint8_t* lds, con
         *reinterpret_cast<float4*>(wo + md * 32 + rr * 8) =
             make_float4(wt.acc_o[md][r], wt.acc_o[md][r + 1], wt.acc_o[md][r + 2], wt.acc_o[md][r + 3]);
       }
-    if (ln.half == 0) {
+    if (half_e == 0) {
       a.ws_ml[slot * 2] = wt.m;
       a.ws_ml[slot * 2 + 1] = l;
     }
   } else if (it.split < 0) {
-    wt.store_out(a.out, q_row, ln.half, col_valid);
+    wt.store_out(a.out, q_row, half_e, col_valid_e);
   } else {
-    finish_piece<D>(a, it.split, it.slot, it.pc & 0xffff, it.pc >> 16, col_valid ? q_row : -1, wt, ln.wave, ln.lane);
+    finish_piece<D>(a, it.split, it.slot, it.pc & 0xffff, it.pc >> 16, col_valid_e ? q_row : -1, wt, ln.wave,
+                    ln.lane);
   }
 }
 

@@ -91,7 +91,9 @@ constexpr int kWaves = kCB;
 constexpr int kThreads = 64 * kWaves;
 // Tile copies: the 128 rows of a tile are 4 row groups of 32; wave w copies
 // row group w % 4 of the V tile (waves 0-3) or of the K tile (waves 4-7).
+// The skewed loop relies on it: the early waves (0-3) are the V copiers.
 constexpr int kRowGroups = 4;
+static_assert(kWaves == 2 * kRowGroups, "early waves copy V rows, late waves K rows");
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4_t lds_short4_t;
