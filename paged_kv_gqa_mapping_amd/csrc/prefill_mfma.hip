@@ -227,11 +227,15 @@ __device__ __forceinline__ void run_item(const PrefillArgs& a, uint8_t* lds, con
         // are requested before its copies (the next barrier's wait covers them)
         TileSource<D>::take(blk, vblk);
         if (kt + 2 < n_kt) vblk = src.fetch_v(kt + 2, ln);
-        // the late waves copy K rows, which the next tile needs first: at once
-        if constexpr (is_late) src.issue(a, lds, ln, blk, kt + 1, kb ^ 1, vnext);
       }
       if constexpr (is_late) {
-        if (kt > kt0 && kt <= n_kt_wave) wt.template pv<false>(lds, ln, vprev);
+        // the late waves copy K rows, which the next tile needs first: at
+        // once, after requesting the first V^T fragments of their P V (LDS
+        // reads, which do not wait for the copies to pass the address path)
+        const bool do_pv = kt > kt0 && kt <= n_kt_wave;
+        if (do_pv) wt.prefetch_v(lds, ln, vprev);
+        if (kt + 1 < n_kt) src.issue(a, lds, ln, blk, kt + 1, kb ^ 1, vnext);
+        if (do_pv) wt.template pv<true>(lds, ln, vprev);
         if (kt < n_kt_wave) wt.template qk_softmax<false>(lds, ln, kb, kt * kKT, 0, pos, min_pos, c);
       } else {
         // the early waves copy V rows, needed only by the next tile's P V:

@@ -387,6 +387,12 @@ struct WaveTile {
     return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 
+  // the first V^T fragments of V buffer vb, requested ahead of pv<true>
+  __device__ __forceinline__ void prefetch_v(const uint8_t* lds, const Lanes<D>& ln, int vb) {
+#pragma unroll
+    for (int j = 0; j < PKV_PREFILL_VPF; ++j) vf[j] = v_frag(lds, ln, vb, j);
+  }
+
   // S^T = K Q^T for K buffer kb, then the online softmax (both below).
   template <bool PRE>
   __device__ __forceinline__ void qk_softmax(const uint8_t* lds, const Lanes<D>& ln, int kb, int key0, int vb, int pos,
