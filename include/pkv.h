@@ -138,16 +138,18 @@ int pkv_rope_kv_store(void* q, const void* k, const void* v, const int32_t* posi
  * workspace, and a reduction pass merges the splits of each (sequence, head).
  * A sequence that fits one split has its output written by the first pass.
  *
- * split_tokens = PKV_SPLIT_BALANCED instead cuts the batch's total context
- * into about 1024 pieces of equal length (at most T tokens, T a multiple of
- * 64 chosen on the device from context_lens; every sequence gets at least
- * one piece), so that the waves of the first pass carry equal work however
- * the context lengths are mixed.
+ * split_tokens = PKV_SPLIT_BALANCED instead cuts the batch's context, taken
+ * as steps of a few tokens sequence after sequence, into up to 1024 ranges of
+ * equal size (one wave each per group of KV heads; each range at least 16
+ * steps, and no sequence in more than 512 ranges), chosen on the device from
+ * context_lens, so that the waves of the first pass carry equal work however
+ * the context lengths are mixed.  A range may end inside one sequence and
+ * cover the start of the next.
  *
- * pkv_decode_split_tokens returns the split the library picks for a shape (a
- * multiple of 64, or PKV_SPLIT_BALANCED where even the longest contexts would
- * give the fixed split at most about 1024 waves, one per SIMD); pass it, or 0
- * for the same choice, or any positive multiple of 64, or PKV_SPLIT_BALANCED.
+ * pkv_decode_split_tokens returns the split the library picks for a shape
+ * (PKV_SPLIT_BALANCED when max_context_len > 256, else max_context_len
+ * rounded up to a multiple of 64: one split per sequence); pass it, or 0 for
+ * the same choice, or any positive multiple of 64, or PKV_SPLIT_BALANCED.
  * pkv_decode_workspace_bytes gives the workspace size that split needs (0
  * when no sequence can span two splits).
  */
@@ -194,8 +196,11 @@ int pkv_paged_decode_attn(const void* q, const void* k_cache, const void* v_cach
  *   process ends.  Nothing is allocated or freed by the call.
  * - A call whose split states need more than that returns PKV_ERR_WORKSPACE
  *   before anything is enqueued (raise split_tokens, or use
- *   pkv_paged_decode_attn).  The states take num_seqs * num_q_heads * S *
- *   (head_dim + 2) * 4 bytes, S = ceil(max_context_len / split).
+ *   pkv_paged_decode_attn).  The states take
+ *   pkv_decode_workspace_bytes(...) bytes: with a fixed split num_seqs *
+ *   num_q_heads * S * (head_dim + 2) * 4, S = ceil(max_context_len / split);
+ *   token-balanced (1024 + num_seqs) * num_q_heads * (head_dim + 2) * 4 +
+ *   8 * num_seqs.
  * - Every call on one GPU shares that GPU's scratch: calls that overlap in
  *   time on one GPU (on different streams, or from several threads without
  *   ordering) race and give undefined results.  Calls ordered on one stream

@@ -86,30 +86,27 @@ int32_t auto_split(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_l
 }
 
 // Token-balanced decode (split_tokens = PKV_SPLIT_BALANCED): the batch's
-// context is cut into about kBalancePieces pieces of equal length (at least
-// one per sequence), one wave each per group of KV heads, so that the waves
-// of a launch carry equal work whatever the mix of context lengths.
+// steps (U tokens each), sequence after sequence, are cut into kBalancePieces
+// ranges of equal size, one wave each per group of KV heads, so that the
+// waves of a launch carry equal work whatever the mix of context lengths; a
+// multiple of the 256 compute units, so that each unit holds as many waves.
 #ifndef PKV_BALANCE_PIECES
 #define PKV_BALANCE_PIECES 1024
 #endif
 constexpr int32_t kBalancePieces = PKV_BALANCE_PIECES;
-int32_t balance_pieces(int32_t num_seqs) { return std::max(num_seqs, kBalancePieces); }
-// states [W, Hq, D] and [W, Hq, 2] floats, then [B, 2] ints of piece bounds
+// states [W + B, Hq, D] and [W + B, Hq, 2] floats (slot w + b for the part of
+// sequence b in wave w's range), then [B, 2] ints (first slot, count)
 int64_t balanced_state_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim) {
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
-  return (int64_t)balance_pieces(num_seqs) * num_q_heads * (head_dim + 2) * (int64_t)sizeof(float) +
+  return ((int64_t)kBalancePieces + num_seqs) * num_q_heads * (head_dim + 2) * (int64_t)sizeof(float) +
          (int64_t)num_seqs * 2 * (int64_t)sizeof(int32_t);
 }
-// The library's choice for split_tokens = 0: equal pieces where even the
-// longest contexts would give the fixed split's grid at most kBalancePieces
-// waves (about one per SIMD), so that the waves of such a small grid finish
-// together; the fixed split otherwise, and one split per sequence for
-// contexts of at most 256 tokens.
+// The library's choice for split_tokens = 0: token-balanced ranges for any
+// context longer than 256 tokens (equal work per wave whatever the mix of
+// lengths; measured faster than the fixed split on every shape tried), and
+// one split per sequence for contexts of at most 256 tokens (auto_split).
 bool auto_balanced(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len) {
-  if (num_seqs < 1 || num_kv_heads < 1 || max_context_len <= 256) return false;
-  const int32_t split = auto_split(num_seqs, num_kv_heads, max_context_len);
-  const int64_t waves = (int64_t)num_seqs * std::max(1, num_kv_heads / 8) * ((max_context_len + split - 1) / split);
-  return waves <= kBalancePieces;
+  return num_seqs >= 1 && num_kv_heads >= 1 && max_context_len > 256;
 }
 
 struct DecodeCall {
@@ -205,7 +202,7 @@ int prepare_decode(DecodeCall& call, const void* q, const void* k_cache, const v
                         : plan   ? plan->split
                         : split_tokens ? split_tokens
                                        : auto_split(num_seqs, num_kv_heads, max_context_len);
-  const int32_t S = balanced ? balance_pieces(num_seqs) : plan ? plan->S : std::max(1, (max_context_len + split - 1) / split);
+  const int32_t S = balanced ? kBalancePieces : plan ? plan->S : std::max(1, (max_context_len + split - 1) / split);
   const int32_t prefix_states = plan ? plan->C : 0;
   const int64_t need = balanced ? balanced_state_bytes(num_seqs, num_q_heads, head_dim)
                                 : state_bytes(num_seqs, num_q_heads, head_dim, S, prefix_states);
@@ -226,7 +223,8 @@ int prepare_decode(DecodeCall& call, const void* q, const void* k_cache, const v
   a.context_lens = context_lens;
   a.out = out;
   a.ws_o = need > 0 ? static_cast<float*>(workspace) : nullptr;
-  const int64_t state_rows = balanced ? (int64_t)S * num_q_heads : (int64_t)num_seqs * num_q_heads * (S + prefix_states);
+  const int64_t state_rows =
+      balanced ? ((int64_t)S + num_seqs) * num_q_heads : (int64_t)num_seqs * num_q_heads * (S + prefix_states);
   a.ws_ml = need > 0 ? a.ws_o + state_rows * head_dim : nullptr;
   if (balanced) {
     a.balance_pieces = S;

@@ -49,11 +49,14 @@ struct RowAttnArgs {
   int32_t num_splits;    // decode: S, the split count of the grid (ceil(max_context_len / split_tokens))
   int32_t max_rows;      // prefill: max_seqlen_q
   // Token-balanced decode (balance_pieces = W > 0 instead of fixed splits):
-  // the batch's total context is cut into at most W pieces of at most T
-  // tokens, T = 64 * ceil(sum_b L_b / (64 * max(W - B, 1))); sequence b gets
-  // n_b = max(1, ceil(L_b / T)) pieces, numbered sequence after sequence.
-  // The states of piece w sit at [w, Hq] of ws_o / ws_ml, and the first
-  // piece of each sequence writes (first piece, n_b) to piece_meta[b].
+  // sequence b is n_b = max(1, ceil(L_b / U)) steps of U tokens; the N steps
+  // of the batch, sequence after sequence, are cut into min(W, N) equal
+  // ranges, wave w (per KV-head group) taking steps [floor(w N / W'),
+  // floor((w + 1) N / W')), W' = min(W, N).
+  // The part of sequence b in wave w's range writes its states at slot w + b
+  // ([w + b, Hq] of ws_o / ws_ml; a sequence's parts have consecutive slots),
+  // and the wave holding b's first step writes (first slot, part count) to
+  // piece_meta[b].
   int32_t balance_pieces;
   int32_t* piece_meta;  // [B, 2]
 };

@@ -120,10 +120,10 @@ hipError_t launch_row_attn(const RowAttnArgs& a, int32_t dtype, int32_t head_dim
 }
 
 hipError_t launch_decode_reduce(const RowAttnArgs& a, int32_t dtype, int32_t head_dim, hipStream_t stream) {
-  const int64_t pairs = (int64_t)a.num_seqs * a.num_q_heads;
-  const int64_t blocks = (pairs + 3) / 4;
-  if (blocks <= 0) return hipSuccess;
-  dim3 grid((unsigned)blocks), block(256);
+  const int64_t pairs = (int64_t)a.num_seqs * a.num_q_heads;  // one workgroup each
+  if (pairs <= 0) return hipSuccess;
+  if (pairs > 0x7fffffff) return hipErrorInvalidValue;
+  dim3 grid((unsigned)pairs), block(kReduceWaves * 64);
   if (dtype == kBF16 && head_dim == 128) hipLaunchKernelGGL((decode_reduce_kernel<true, 128>), grid, block, 0, stream, a);
   else if (dtype == kBF16 && head_dim == 64) hipLaunchKernelGGL((decode_reduce_kernel<true, 64>), grid, block, 0, stream, a);
   else if (dtype == kF32 && head_dim == 128) hipLaunchKernelGGL((decode_reduce_kernel<false, 128>), grid, block, 0, stream, a);

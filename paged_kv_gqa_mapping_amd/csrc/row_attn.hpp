@@ -89,54 +89,114 @@ __device__ __forceinline__ void store_words(char* p, const uint32_t* w) {
   *reinterpret_cast<T*>(p) = x;
 }
 
-// Wave-wide sum and inclusive prefix sum (64 lanes).
+// Wave-wide sum (64 lanes).
 __device__ __forceinline__ long long wave_sum_i64(long long x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
   return x;
 }
-__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
+
+// Token-balanced decode (see RowAttnArgs): sequence b is n_b = max(1,
+// ceil(L_b / U)) steps of U tokens (an empty context counts one step, which
+// writes its row of zeros); the batch's N steps, sequence after sequence, are
+// cut into W <= N ranges of equal size (none empty), wave w taking
+// [floor(w N / W), floor((w + 1) N / W)).  A range may cross sequences: each (wave, sequence)
+// pair it touches is a segment, whose state goes to slot w + b.  Along the
+// step order w + b grows by at least one per segment, so the segments of one
+// sequence sit in consecutive slots, all below W + B.
+__device__ __forceinline__ long long steps_of(int L, int U) { return max(1, (max(L, 0) + U - 1) / U); }
+// the wave whose range holds step x, 0 <= x < N
+__device__ __forceinline__ int wave_of_step(long long x, long long N, int W) {
+  return (int)(((x + 1) * (long long)W - 1) / N);
+}
+__device__ __forceinline__ long long readlane_i64(long long x, int src) {
+  const int lo = __builtin_amdgcn_readlane((int)(unsigned)(x & 0xffffffffLL), src);
+  const int hi = __builtin_amdgcn_readlane((int)(x >> 32), src);
+  return (long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo);
+}
+__device__ __forceinline__ long long wave_inclusive_scan_i64(long long x, int lane) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
+    const long long y = __shfl_up(x, o);
     if (lane >= o) x += y;
   }
   return x;
 }
-
-// Token-balanced decode: the piece a wave works on (see RowAttnArgs).  Every
-// wave derives the same piece boundaries from context_lens: the total (one
-// pass over the lengths), then each sequence's piece count and a running
-// prefix sum until the sequence holding piece w.  Returns false past the
-// last piece.
-__device__ __forceinline__ bool balanced_piece(const RowAttnArgs& a, int w, int lane, int& b, int& j, int& off_b,
-                                               int& n_b, int& len_b) {
-  const int B = a.num_seqs;
-  long long tot = 0;
-  for (int i = lane; i < B; i += 64) tot += max(a.context_lens[i], 0);
-  tot = wave_sum_i64(tot);
-  const long long room = max((long long)a.balance_pieces - B, 1LL);
-  const long long per = (tot + room - 1) / room;
-  const int T = (int)min(max(64LL, (per + 63) / 64 * 64), (long long)0x40000000);
-  int base = 0;
-  for (int i0 = 0; i0 < B; i0 += 64) {
-    const int i = i0 + lane;
-    const int L = i < B ? max(a.context_lens[i], 0) : 0;
-    const int n = i < B ? max(1, (L + T - 1) / T) : 0;
-    const int incl = wave_inclusive_scan(n, lane);
-    const int off = base + incl - n;
-    const uint64_t hit = __builtin_amdgcn_ballot_w64(i < B && off <= w && w < off + n);
-    if (hit) {
-      const int src = __builtin_ctzll(hit);
-      b = i0 + src;
-      off_b = __builtin_amdgcn_readlane(off, src);
-      n_b = __builtin_amdgcn_readlane(n, src);
-      const int Lb = __builtin_amdgcn_readlane(L, src);
-      len_b = ((Lb + n_b - 1) / n_b + 63) / 64 * 64;
-      j = w - off_b;
-      return true;
+// Total steps N of the batch, and the sequence b holding step s (< N) with
+// its first step base, which every wave derives from context_lens.  The
+// lengths are read kScanBatch * 64 at a time (one memory round trip for that
+// many sequences); the first batch's stay in registers for the search.
+constexpr int kScanBatch = 4;
+struct StepScan {
+  int L[kScanBatch];        // context lengths of sequences lane + 64 k
+  long long n[kScanBatch];  // their steps (0 past the end)
+};
+__device__ __forceinline__ void scan_load(const RowAttnArgs& a, int U, int i0, int lane, StepScan& sc) {
+#pragma unroll
+  for (int k = 0; k < kScanBatch; ++k) {
+    const int i = i0 + 64 * k + lane;
+    sc.L[k] = i < a.num_seqs ? max(a.context_lens[i], 0) : 0;
+  }
+#pragma unroll
+  for (int k = 0; k < kScanBatch; ++k) sc.n[k] = i0 + 64 * k + lane < a.num_seqs ? steps_of(sc.L[k], U) : 0;
+}
+// N, and the most steps of any one sequence in nmax.
+__device__ __forceinline__ long long total_steps(const RowAttnArgs& a, int U, int lane, StepScan& first,
+                                                 long long& nmax) {
+  long long n = 0, mx = 0;
+  scan_load(a, U, 0, lane, first);
+#pragma unroll
+  for (int k = 0; k < kScanBatch; ++k) {
+    n += first.n[k];
+    mx = max(mx, first.n[k]);
+  }
+  for (int i0 = 64 * kScanBatch; i0 < a.num_seqs; i0 += 64 * kScanBatch) {
+    StepScan sc;
+    scan_load(a, U, i0, lane, sc);
+#pragma unroll
+    for (int k = 0; k < kScanBatch; ++k) {
+      n += sc.n[k];
+      mx = max(mx, sc.n[k]);
     }
-    base += __builtin_amdgcn_readlane(incl, 63);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = max(mx, (long long)__shfl_xor(mx, o));
+  nmax = mx;
+  return wave_sum_i64(n);
+}
+// Waves of a token-balanced launch: at most W, at least kMinSteps steps each
+// (shorter ranges cost more in per-wave start-up and states than they save),
+// and no sequence cut into more than kMaxParts parts (its merge reads at most
+// 64 states per wave of the reduction).  Never more than N, so no range is
+// empty.
+constexpr int kMinSteps = 16;
+constexpr int kMaxParts = 512;
+__device__ __forceinline__ int balanced_waves(int W, long long N, long long nmax) {
+  long long w = min((long long)W, max(1LL, N / kMinSteps));
+  w = min(w, max(1LL, kMaxParts * N / max(nmax, 1LL)));
+  return (int)min(w, N);
+}
+__device__ __forceinline__ bool sequence_of_step(const RowAttnArgs& a, int U, long long s, int lane,
+                                                 const StepScan& first, int& b, long long& base, int& L) {
+  long long run = 0;
+  StepScan sc = first;
+  for (int i0 = 0; i0 < a.num_seqs; i0 += 64 * kScanBatch) {
+    if (i0 > 0) scan_load(a, U, i0, lane, sc);
+#pragma unroll
+    for (int k = 0; k < kScanBatch; ++k) {
+      const long long n = sc.n[k];
+      const long long incl = wave_inclusive_scan_i64(n, lane);
+      const long long off = run + incl - n;
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(n > 0 && off <= s && s < off + n);
+      if (hit) {
+        const int src = __builtin_ctzll(hit);
+        b = i0 + 64 * k + src;
+        base = readlane_i64(off, src);
+        L = __builtin_amdgcn_readlane(sc.L[k], src);
+        return true;
+      }
+      run += readlane_i64(incl, 63);
+    }
   }
   return false;
 }
@@ -163,332 +223,368 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
   int item = blockIdx.x;
   const int hg = item % n_hg;
   item /= n_hg;
-  // decode pieces: split j_or_row of sequence b, fixed length or token-balanced
-  const bool balanced = !PREFILL && a.balance_pieces > 0;
-  int b, j_or_row, off_b = 0, n_bal = 1, len_b = 0;
-  if (balanced) {
-    if (!balanced_piece(a, item, lane, b, j_or_row, off_b, n_bal, len_b)) return;
-  } else {
-    b = item % a.num_seqs;
-    j_or_row = item / a.num_seqs;
-  }
   const int g = hg * HPW + hl;
   const int Hq = a.num_q_heads;
   const int Hkv = a.num_kv_heads;
   const int64_t row_bytes = (int64_t)Hkv * D * ELT;
-
-  // This wave's query row, its key range [t0, t1), and the split index.
-  int64_t q_row;
-  int t0, t1, split = 0, nsplit_b = 1, k0 = 0;
-  int t_new = -1;  // fused store: position of the newest token if this wave's range holds it
-  int t_fin = -1;  // fused store: first token of the step that holds it
-  if constexpr (PREFILL) {
-    const int qb = a.cu_seqlens_q[b];
-    const int lq = a.cu_seqlens_q[b + 1] - qb;
-    const int i = lq - 1 - j_or_row;  // longest rows first
-    if (i < 0) return;
-    k0 = a.cu_seqlens_k[b];
-    const int lk = a.cu_seqlens_k[b + 1] - k0;
-    q_row = qb + i;
-    t0 = 0;
-    t1 = lk - lq + i + 1;
-  } else {
-    // keys [0, start) of a sequence with a shared prefix belong to the group pass
-    const int L = a.context_lens[b];
-    const int start = a.kv_start ? a.kv_start[b] : 0;
-    split = j_or_row;
-    q_row = b;
-    const int piece = balanced ? len_b : a.split_tokens;
-    t0 = start + split * piece;
-    if (L == 0) {
-      if (split == 0) {  // an empty context gives zeros
-        for (int gq = 0; gq < G; ++gq) {
-          char* op = (char*)a.out + ((q_row * Hq + g * G + gq) * D) * ELT + c * CH;
-          uint32_t z[WPC] = {};
-          for (int jj = 0; jj < NCH; ++jj) store_words<CH>(op + jj * TL * CH, z);
-        }
-      }
-      return;
-    }
-    if (t0 >= L) return;
-    t1 = min(L, t0 + piece);
-    if (STORE && t1 == L) {
-      // the step holding the newest token is taken out of the streaming loop
-      // and done after it, with that token read from k_new / v_new
-      t_new = L - 1;
-      t_fin = t0 + (t_new - t0) / U * U;
-      t1 = t_fin;
-    }
-    // states merged for this row: its splits, plus the group pass's when it has a prefix
-    nsplit_b = balanced ? n_bal : (L - start + a.split_tokens - 1) / a.split_tokens + (start > 0 ? 1 : 0);
-    if (balanced && split == 0 && hg == 0 && lane == 0) {
-      a.piece_meta[2 * b] = off_b;
-      a.piece_meta[2 * b + 1] = n_bal;
-    }
-  }
-
-  // Queries of the G heads sharing KV head g, in this lane's element order.
-  // Scores are scaled by c >= 0 (a negative scale is applied by negating q,
-  // which is exact, and using |c|).
-  uint32_t qw[G][NW];
-  for (int gq = 0; gq < G; ++gq) {
-    const char* qp = (const char*)a.q + ((q_row * Hq + g * G + gq) * D) * ELT + c * CH;
-    for (int jj = 0; jj < NCH; ++jj) load_words<CH>(&qw[gq][jj * WPC], qp + jj * TL * CH);
-  }
-  float cs = a.scale_log2;
-  if (cs < 0.f) {
-    const uint32_t sign = BF16 ? 0x80008000u : 0x80000000u;
-    for (int gq = 0; gq < G; ++gq)
-      for (int w = 0; w < NW; ++w) qw[gq][w] ^= sign;
-    cs = -cs;
-  }
-
-  float m[G], l[G], o[G][DPL];
-  for (int gq = 0; gq < G; ++gq) {
-    m[gq] = kNegInf;
-    l[gq] = 0.f;
-    for (int e = 0; e < DPL; ++e) o[gq][e] = 0.f;
-  }
-
-  const int32_t* table = a.block_tables ? a.block_tables + (int64_t)b * a.max_blocks_per_seq : nullptr;
-  const int bs_mask = (1 << a.log2_block_size) - 1;
-  const char* kbase = (const char*)a.k;
-  const char* vbase = (const char*)a.v;
-  const int lane_off = g * D * ELT + c * CH;
-
-  // Row index of the first token of a step (U tokens never straddle a block:
-  // steps start at multiples of U and U divides the block size).  Block ids
-  // come from a 64-entry window of the table held one per lane and read with
-  // readlane, so a lookup costs no memory round trip; the window moves when a
-  // step leaves it.
-  int win0 = -(1 << 30);  // first block index of the window
-  int win = 0;          // this lane's entry: table[win0 + lane]
-  auto step_row = [&](int t) -> int64_t {
-    if (table) {
-      const int bi = t >> a.log2_block_size;
-      if (bi - win0 >= 64 || bi < win0) {
-        win0 = bi;
-        const int e = bi + lane;
-        win = e < a.max_blocks_per_seq ? table[e] : 0;
-      }
-      const int64_t blk = __builtin_amdgcn_readlane(win, bi - win0);
-      return (blk << a.log2_block_size) + (t & bs_mask);
-    }
-    return (int64_t)k0 + t;
-  };
-
-  struct Buf {
-    uint32_t k[U][NW];
-    uint32_t v[U][NW];
-  };
-  auto load = [&](Buf& buf, int t) {
-    const int64_t r0 = step_row(t);
-    const int last = t1 - 1 - t;  // tokens past the end re-read the last valid row
-    for (int u = 0; u < U; ++u) {
-      const int64_t r = r0 + min(u, last);
-      const char* kp = kbase + r * row_bytes + lane_off;
-      const char* vp = vbase + r * row_bytes + lane_off;
-      for (int jj = 0; jj < NCH; ++jj) {
-        load_stream<CH>(&buf.k[u][jj * WPC], kp + jj * TL * CH);
-        load_stream<CH>(&buf.v[u][jj * WPC], vp + jj * TL * CH);
-      }
-    }
-  };
-  static_assert(!BF16 || U % 2 == 0, "bf16 steps pair tokens");
   const uint32_t kOnes = 0x3F803F80u;  // bf16 pair (1, 1)
-  auto compute = [&](const Buf& buf, int t) {
-    float s[U][G];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-#pragma unroll
-      for (int gq = 0; gq < G; ++gq) {
-        float acc = 0.f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          if constexpr (BF16) {
-            acc = dot2_bf16(qw[gq][w], buf.k[u][w], acc);
-          } else {
-            acc = fmaf(__uint_as_float(qw[gq][w]), __uint_as_float(buf.k[u][w]), acc);
-          }
-        }
-        s[u][gq] = group_sum<TL>(acc) * cs;
-      }
-    }
-    // tokens past the end (last step only): they take token 0's score for the
-    // max and get weight 0 below
-    const int nvalid = t1 - t;
-    if (nvalid < U) {
-#pragma unroll
-      for (int u = 1; u < U; ++u)
-        if (u >= nvalid)
-#pragma unroll
-          for (int gq = 0; gq < G; ++gq) s[u][gq] = s[0][gq];
-    }
-    bool raise = false;
-    float mx[G];
-#pragma unroll
+  static_assert(!BF16 || U % 2 == 0, "bf16 steps pair tokens");
+
+  // Zeros for the G query heads of this lane group (a decode row with an empty context).
+  auto write_zeros = [&](int64_t q_row) {
     for (int gq = 0; gq < G; ++gq) {
-      mx[gq] = s[0][gq];
-#pragma unroll
-      for (int u = 1; u < U; ++u) mx[gq] = fmaxf(mx[gq], s[u][gq]);
-      raise |= mx[gq] > m[gq] + kTau;
+      char* op = (char*)a.out + ((q_row * Hq + g * G + gq) * D) * ELT + c * CH;
+      uint32_t z[WPC] = {};
+      for (int jj = 0; jj < NCH; ++jj) store_words<CH>(op + jj * TL * CH, z);
     }
-    if (wave_any(raise)) {
-#pragma unroll
-      for (int gq = 0; gq < G; ++gq) {
-        const float mn = fmaxf(m[gq], mx[gq]);
-        const float alpha = exp2_hw(m[gq] - mn);
-        m[gq] = mn;
-        l[gq] *= alpha;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) o[gq][e] *= alpha;
+  };
+
+  // One segment: keys [t0, t1) of query row q_row (sequence b; prefill rows
+  // read packed rows from k0).  nstates == 1: the normalised output is
+  // written; else the unnormalised state goes to slots sbase + (query head) *
+  // sstride.  L_store: the context length, for the fused store of the newest
+  // token (decode with STORE only).
+  auto segment = [&](int b, int64_t q_row, int t0, int t1, int k0, int L_store, int nstates, int64_t sbase,
+                     int sstride) {
+    int t_new = -1;  // fused store: position of the newest token if this segment holds it
+    int t_fin = -1;  // fused store: first token of the step that holds it
+    if constexpr (STORE && !PREFILL) {
+      if (t1 == L_store) {
+        // the step holding the newest token is taken out of the streaming loop
+        // and done after it, with that token read from k_new / v_new
+        t_new = L_store - 1;
+        t_fin = t0 + (t_new - t0) / U * U;
+        t1 = t_fin;
       }
     }
-    float p[U][G];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int gq = 0; gq < G; ++gq) p[u][gq] = exp2_hw(s[u][gq] - m[gq]);  // the max token gets exactly 1
-    if (nvalid < U) {
-#pragma unroll
-      for (int u = 1; u < U; ++u)
-        if (u >= nvalid)
-#pragma unroll
-          for (int gq = 0; gq < G; ++gq) p[u][gq] = 0.f;
+
+    // Queries of the G heads sharing KV head g, in this lane's element order.
+    // Scores are scaled by c >= 0 (a negative scale is applied by negating q,
+    // which is exact, and using |c|).
+    uint32_t qw[G][NW];
+    for (int gq = 0; gq < G; ++gq) {
+      const char* qp = (const char*)a.q + ((q_row * Hq + g * G + gq) * D) * ELT + c * CH;
+      for (int jj = 0; jj < NCH; ++jj) load_words<CH>(&qw[gq][jj * WPC], qp + jj * TL * CH);
     }
-    if constexpr (BF16) {
-      // weights of two tokens as one bf16 pair; V of the two tokens interleaved
-      // per element, so each v_dot2 adds both tokens' terms of one element.
-#pragma unroll
-      for (int u = 0; u < U; u += 2) {
-        uint32_t pp[G];
-#pragma unroll
-        for (int gq = 0; gq < G; ++gq) {
-          pp[gq] = pack_bf16x2(p[u][gq], p[u + 1][gq]);
-          l[gq] = dot2_bf16(pp[gq], kOnes, l[gq]);
+    float cs = a.scale_log2;
+    if (cs < 0.f) {
+      const uint32_t sign = BF16 ? 0x80008000u : 0x80000000u;
+      for (int gq = 0; gq < G; ++gq)
+        for (int w = 0; w < NW; ++w) qw[gq][w] ^= sign;
+      cs = -cs;
+    }
+
+    float m[G], l[G], o[G][DPL];
+    for (int gq = 0; gq < G; ++gq) {
+      m[gq] = kNegInf;
+      l[gq] = 0.f;
+      for (int e = 0; e < DPL; ++e) o[gq][e] = 0.f;
+    }
+
+    const int32_t* table = a.block_tables ? a.block_tables + (int64_t)b * a.max_blocks_per_seq : nullptr;
+    const int bs_mask = (1 << a.log2_block_size) - 1;
+    const char* kbase = (const char*)a.k;
+    const char* vbase = (const char*)a.v;
+    const int lane_off = g * D * ELT + c * CH;
+
+    // Row index of the first token of a step (U tokens never straddle a block:
+    // steps start at multiples of U and U divides the block size).  Block ids
+    // come from a 64-entry window of the table held one per lane and read with
+    // readlane, so a lookup costs no memory round trip; the window moves when a
+    // step leaves it.
+    int win0 = -(1 << 30);  // first block index of the window
+    int win = 0;          // this lane's entry: table[win0 + lane]
+    auto step_row = [&](int t) -> int64_t {
+      if (table) {
+        const int bi = t >> a.log2_block_size;
+        if (bi - win0 >= 64 || bi < win0) {
+          win0 = bi;
+          const int e = bi + lane;
+          win = e < a.max_blocks_per_seq ? table[e] : 0;
         }
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          // v_perm_b32: selector bytes 0-3 pick from the second operand, 4-7 from the first
-          const uint32_t a0 = buf.v[u][w], a1 = buf.v[u + 1][w];
-          const uint32_t lo = __builtin_amdgcn_perm(a1, a0, 0x05040100u);  // (a0.lo, a1.lo)
-          const uint32_t hi = __builtin_amdgcn_perm(a1, a0, 0x07060302u);  // (a0.hi, a1.hi)
-#pragma unroll
-          for (int gq = 0; gq < G; ++gq) {
-            o[gq][2 * w] = dot2_bf16(pp[gq], lo, o[gq][2 * w]);
-            o[gq][2 * w + 1] = dot2_bf16(pp[gq], hi, o[gq][2 * w + 1]);
-          }
+        const int64_t blk = __builtin_amdgcn_readlane(win, bi - win0);
+        return (blk << a.log2_block_size) + (t & bs_mask);
+      }
+      return (int64_t)k0 + t;
+    };
+
+    struct Buf {
+      uint32_t k[U][NW];
+      uint32_t v[U][NW];
+    };
+    auto load = [&](Buf& buf, int t) {
+      const int64_t r0 = step_row(t);
+      const int last = t1 - 1 - t;  // tokens past the end re-read the last valid row
+      for (int u = 0; u < U; ++u) {
+        const int64_t r = r0 + min(u, last);
+        const char* kp = kbase + r * row_bytes + lane_off;
+        const char* vp = vbase + r * row_bytes + lane_off;
+        for (int jj = 0; jj < NCH; ++jj) {
+          load_stream<CH>(&buf.k[u][jj * WPC], kp + jj * TL * CH);
+          load_stream<CH>(&buf.v[u][jj * WPC], vp + jj * TL * CH);
         }
       }
-    } else {
+    };
+    auto compute = [&](const Buf& buf, int t) {
+      float s[U][G];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
 #pragma unroll
-        for (int gq = 0; gq < G; ++gq) l[gq] += p[u][gq];
+        for (int gq = 0; gq < G; ++gq) {
+          float acc = 0.f;
 #pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          const float v0 = __uint_as_float(buf.v[u][w]);
+          for (int w = 0; w < NW; ++w) {
+            if constexpr (BF16) {
+              acc = dot2_bf16(qw[gq][w], buf.k[u][w], acc);
+            } else {
+              acc = fmaf(__uint_as_float(qw[gq][w]), __uint_as_float(buf.k[u][w]), acc);
+            }
+          }
+          s[u][gq] = group_sum<TL>(acc) * cs;
+        }
+      }
+      // tokens past the end (last step only): they take token 0's score for the
+      // max and get weight 0 below
+      const int nvalid = t1 - t;
+      if (nvalid < U) {
 #pragma unroll
-          for (int gq = 0; gq < G; ++gq) o[gq][w] = fmaf(p[u][gq], v0, o[gq][w]);
+        for (int u = 1; u < U; ++u)
+          if (u >= nvalid)
+#pragma unroll
+            for (int gq = 0; gq < G; ++gq) s[u][gq] = s[0][gq];
+      }
+      bool raise = false;
+      float mx[G];
+#pragma unroll
+      for (int gq = 0; gq < G; ++gq) {
+        mx[gq] = s[0][gq];
+#pragma unroll
+        for (int u = 1; u < U; ++u) mx[gq] = fmaxf(mx[gq], s[u][gq]);
+        raise |= mx[gq] > m[gq] + kTau;
+      }
+      if (wave_any(raise)) {
+#pragma unroll
+        for (int gq = 0; gq < G; ++gq) {
+          const float mn = fmaxf(m[gq], mx[gq]);
+          const float alpha = exp2_hw(m[gq] - mn);
+          m[gq] = mn;
+          l[gq] *= alpha;
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) o[gq][e] *= alpha;
+        }
+      }
+      float p[U][G];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int gq = 0; gq < G; ++gq) p[u][gq] = exp2_hw(s[u][gq] - m[gq]);  // the max token gets exactly 1
+      if (nvalid < U) {
+#pragma unroll
+        for (int u = 1; u < U; ++u)
+          if (u >= nvalid)
+#pragma unroll
+            for (int gq = 0; gq < G; ++gq) p[u][gq] = 0.f;
+      }
+      if constexpr (BF16) {
+        // weights of two tokens as one bf16 pair; V of the two tokens interleaved
+        // per element, so each v_dot2 adds both tokens' terms of one element.
+#pragma unroll
+        for (int u = 0; u < U; u += 2) {
+          uint32_t pp[G];
+#pragma unroll
+          for (int gq = 0; gq < G; ++gq) {
+            pp[gq] = pack_bf16x2(p[u][gq], p[u + 1][gq]);
+            l[gq] = dot2_bf16(pp[gq], kOnes, l[gq]);
+          }
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            // v_perm_b32: selector bytes 0-3 pick from the second operand, 4-7 from the first
+            const uint32_t a0 = buf.v[u][w], a1 = buf.v[u + 1][w];
+            const uint32_t lo = __builtin_amdgcn_perm(a1, a0, 0x05040100u);  // (a0.lo, a1.lo)
+            const uint32_t hi = __builtin_amdgcn_perm(a1, a0, 0x07060302u);  // (a0.hi, a1.hi)
+#pragma unroll
+            for (int gq = 0; gq < G; ++gq) {
+              o[gq][2 * w] = dot2_bf16(pp[gq], lo, o[gq][2 * w]);
+              o[gq][2 * w + 1] = dot2_bf16(pp[gq], hi, o[gq][2 * w + 1]);
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+          for (int gq = 0; gq < G; ++gq) l[gq] += p[u][gq];
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            const float v0 = __uint_as_float(buf.v[u][w]);
+#pragma unroll
+            for (int gq = 0; gq < G; ++gq) o[gq][w] = fmaf(p[u][gq], v0, o[gq][w]);
+          }
+        }
+      }
+    };
+
+    // A ring of R step buffers: the loads of step s + R - 1 are issued before
+    // step s is computed, so R - 1 steps of K/V rows are in flight per wave.
+    const int nsteps = (t1 - t0 + U - 1) / U;
+    Buf ring[R];
+#pragma unroll
+    for (int r = 0; r < R - 1; ++r)
+      if (r < nsteps) load(ring[r], t0 + r * U);
+    for (int st = 0; st < nsteps; st += R) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int s = st + r;
+        if (s >= nsteps) break;
+        if (s + R - 1 < nsteps) load(ring[(r + R - 1) % R], t0 + (s + R - 1) * U);
+        compute(ring[r], t0 + s * U);
+      }
+    }
+
+    if constexpr (STORE && !PREFILL) {
+      // fused store: the last step, with the same token boundaries as when
+      // streamed, so the result has the same bits as storing first; its older
+      // tokens come from the cache, the newest token and its past-the-end copies
+      // from k_new / v_new, and the newest token is written to its cache row
+      if (t_new >= 0) {
+        t1 = t_new + 1;
+        Buf fb;
+        load(fb, t_fin);
+        const int un = t_new - t_fin;
+        uint32_t nk[NW], nv[NW];
+        const char* kn = (const char*)a.k_new + (int64_t)b * row_bytes + lane_off;
+        const char* vn = (const char*)a.v_new + (int64_t)b * row_bytes + lane_off;
+        for (int jj = 0; jj < NCH; ++jj) {
+          load_words<CH>(&nk[jj * WPC], kn + jj * TL * CH);
+          load_words<CH>(&nv[jj * WPC], vn + jj * TL * CH);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (u >= un)
+#pragma unroll
+            for (int w = 0; w < NW; ++w) {
+              fb.k[u][w] = nk[w];
+              fb.v[u][w] = nv[w];
+            }
+        const int64_t r = step_row(t_new);
+        for (int jj = 0; jj < NCH; ++jj) {
+          store_words<CH>((char*)a.k + r * row_bytes + lane_off + jj * TL * CH, &nk[jj * WPC]);
+          store_words<CH>((char*)a.v + r * row_bytes + lane_off + jj * TL * CH, &nv[jj * WPC]);
+        }
+        compute(fb, t_fin);
+      }
+    }
+
+    if (nstates == 1) {
+      for (int gq = 0; gq < G; ++gq) {
+        const float inv = 1.0f / l[gq];
+        char* op = (char*)a.out + ((q_row * Hq + g * G + gq) * D) * ELT + c * CH;
+        for (int jj = 0; jj < NCH; ++jj) {
+          uint32_t w[WPC];
+          for (int x = 0; x < WPC; ++x) {
+            const int e = (jj * WPC + x) * EPW;
+            if constexpr (BF16) {
+              w[x] = pack_bf16x2(o[gq][e] * inv, o[gq][e + 1] * inv);
+            } else {
+              w[x] = __float_as_uint(o[gq][e] * inv);
+            }
+          }
+          store_words<CH>(op + jj * TL * CH, w);
+        }
+      }
+    } else {
+      for (int gq = 0; gq < G; ++gq) {
+        const int64_t slot = sbase + (int64_t)(g * G + gq) * sstride;
+        float* wo = a.ws_o + slot * D;
+        for (int jj = 0; jj < NCH; ++jj) {
+          const int d0 = (jj * TL + c) * EPC;
+          for (int x = 0; x < EPC; ++x) wo[d0 + x] = o[gq][jj * EPC + x];
+        }
+        if (c == 0) {
+          a.ws_ml[slot * 2] = m[gq];
+          a.ws_ml[slot * 2 + 1] = l[gq];
         }
       }
     }
   };
 
-  // A ring of R step buffers: the loads of step s + R - 1 are issued before
-  // step s is computed, so R - 1 steps of K/V rows are in flight per wave.
-  const int nsteps = (t1 - t0 + U - 1) / U;
-  Buf ring[R];
-#pragma unroll
-  for (int r = 0; r < R - 1; ++r)
-    if (r < nsteps) load(ring[r], t0 + r * U);
-  for (int st = 0; st < nsteps; st += R) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      const int s = st + r;
-      if (s >= nsteps) break;
-      if (s + R - 1 < nsteps) load(ring[(r + R - 1) % R], t0 + (s + R - 1) * U);
-      compute(ring[r], t0 + s * U);
-    }
-  }
-
-  if constexpr (STORE && !PREFILL) {
-    // fused store: the last step, with the same token boundaries as when
-    // streamed, so the result has the same bits as storing first; its older
-    // tokens come from the cache, the newest token and its past-the-end copies
-    // from k_new / v_new, and the newest token is written to its cache row
-    if (t_new >= 0) {
-      t1 = t_new + 1;
-      Buf fb;
-      load(fb, t_fin);
-      const int un = t_new - t_fin;
-      uint32_t nk[NW], nv[NW];
-      const char* kn = (const char*)a.k_new + (int64_t)b * row_bytes + lane_off;
-      const char* vn = (const char*)a.v_new + (int64_t)b * row_bytes + lane_off;
-      for (int jj = 0; jj < NCH; ++jj) {
-        load_words<CH>(&nk[jj * WPC], kn + jj * TL * CH);
-        load_words<CH>(&nv[jj * WPC], vn + jj * TL * CH);
+  if constexpr (PREFILL) {
+    // prefill row i of sequence b (longest rows first): keys 0 .. Lk - Lq + i
+    const int b = item % a.num_seqs;
+    const int qb = a.cu_seqlens_q[b];
+    const int lq = a.cu_seqlens_q[b + 1] - qb;
+    const int i = lq - 1 - item / a.num_seqs;
+    if (i < 0) return;
+    const int k0 = a.cu_seqlens_k[b];
+    const int lk = a.cu_seqlens_k[b + 1] - k0;
+    segment(b, qb + i, 0, lk - lq + i + 1, k0, 0, 1, 0, 0);
+  } else if (a.balance_pieces > 0) {
+    // token-balanced: the segments of this wave's range of steps (no range is
+    // empty, so the parts of a sequence sit in consecutive waves)
+    const int w = item;
+    StepScan first;
+    long long nmax;
+    const long long N = total_steps(a, U, lane, first, nmax);
+    const int W = balanced_waves(a.balance_pieces, N, nmax);
+    if (w >= W) return;
+    const long long s_lo = (long long)w * N / W, s_hi = (long long)(w + 1) * N / W;
+    int b, L;
+    long long base;
+    if (!sequence_of_step(a, U, s_lo, lane, first, b, base, L)) return;
+    for (long long s = s_lo; s < s_hi && b < a.num_seqs; ++b) {
+      if (s > s_lo) L = max(a.context_lens[b], 0);
+      const long long n = steps_of(L, U);
+      const long long e = min(s_hi, base + n);
+      const int w0 = wave_of_step(base, N, W);
+      const int nst = wave_of_step(base + n - 1, N, W) - w0 + 1;
+      if (s == base && hg == 0 && lane == 0) {
+        a.piece_meta[2 * b] = w0 + b;
+        a.piece_meta[2 * b + 1] = nst;
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (u >= un)
-#pragma unroll
-          for (int w = 0; w < NW; ++w) {
-            fb.k[u][w] = nk[w];
-            fb.v[u][w] = nv[w];
-          }
-      const int64_t r = step_row(t_new);
-      for (int jj = 0; jj < NCH; ++jj) {
-        store_words<CH>((char*)a.k + r * row_bytes + lane_off + jj * TL * CH, &nk[jj * WPC]);
-        store_words<CH>((char*)a.v + r * row_bytes + lane_off + jj * TL * CH, &nv[jj * WPC]);
+      if (L == 0) {
+        write_zeros(b);
+      } else {
+        segment(b, b, (int)((s - base) * U), (int)min((long long)L, (e - base) * U), 0, L, nst,
+                (int64_t)(w + b) * Hq, 1);
       }
-      compute(fb, t_fin);
-    }
-  }
-
-  if (nsplit_b == 1) {
-    for (int gq = 0; gq < G; ++gq) {
-      const float inv = 1.0f / l[gq];
-      char* op = (char*)a.out + ((q_row * Hq + g * G + gq) * D) * ELT + c * CH;
-      for (int jj = 0; jj < NCH; ++jj) {
-        uint32_t w[WPC];
-        for (int x = 0; x < WPC; ++x) {
-          const int e = (jj * WPC + x) * EPW;
-          if constexpr (BF16) {
-            w[x] = pack_bf16x2(o[gq][e] * inv, o[gq][e + 1] * inv);
-          } else {
-            w[x] = __float_as_uint(o[gq][e] * inv);
-          }
-        }
-        store_words<CH>(op + jj * TL * CH, w);
-      }
+      s = e;
+      base += n;
     }
   } else {
-    const int S = a.ws_stride;
-    for (int gq = 0; gq < G; ++gq) {
-      const int64_t slot = balanced ? (int64_t)(off_b + split) * Hq + g * G + gq
-                                    : ((int64_t)b * Hq + g * G + gq) * S + split;
-      float* wo = a.ws_o + slot * D;
-      for (int jj = 0; jj < NCH; ++jj) {
-        const int d0 = (jj * TL + c) * EPC;
-        for (int x = 0; x < EPC; ++x) wo[d0 + x] = o[gq][jj * EPC + x];
-      }
-      if (c == 0) {
-        a.ws_ml[slot * 2] = m[gq];
-        a.ws_ml[slot * 2 + 1] = l[gq];
-      }
+    // split j of sequence b; keys [0, start) of a sequence with a shared
+    // prefix belong to the group pass
+    const int b = item % a.num_seqs;
+    const int split = item / a.num_seqs;
+    const int L = a.context_lens[b];
+    const int start = a.kv_start ? a.kv_start[b] : 0;
+    if (L == 0) {
+      if (split == 0) write_zeros(b);  // an empty context gives zeros
+      return;
     }
+    const int t0 = start + split * a.split_tokens;
+    if (t0 >= L) return;
+    // states merged for this row: its splits, plus the group pass's when it has a prefix
+    const int nst = (L - start + a.split_tokens - 1) / a.split_tokens + (start > 0 ? 1 : 0);
+    const int S = a.ws_stride;
+    segment(b, b, t0, min(L, t0 + a.split_tokens), 0, L, nst, (int64_t)b * Hq * S + split, S);
   }
 }
 
 // Merge the split states of each (sequence, query head): M = max_j m_j,
-// w_j = 2^(m_j - M), out = sum_j w_j o_j / sum_j w_j l_j.  One wave per pair,
-// states merged in slot order: the pair's splits, then the group pass's
-// chunks of its shared prefix (if any).
+// w_j = 2^(m_j - M), out = sum_j w_j o_j / sum_j w_j l_j, over the pair's
+// states in slot order: its splits (or token-balanced parts), then the group
+// pass's chunks of its shared prefix (if any).  One workgroup per pair; its
+// n states are cut into nw = min(kReduceWaves, ceil(n / 8)) consecutive
+// slices, one per wave, and each wave merges its slice as above (reading the
+// states eight at a time, combining them one by one); with nw > 1 the slice
+// results are then merged the same way, in slice order.
+constexpr int kReduceWaves = 8;
 template <bool BF16, int D>
-__global__ __launch_bounds__(256) void decode_reduce_kernel(RowAttnArgs a) {
+__global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce_kernel(RowAttnArgs a) {
   constexpr int EPL = D / 64;  // elements per lane
-  const int pair = blockIdx.x * 4 + threadIdx.x / 64;
+  constexpr int kBatch = 8;
+  const int pair = blockIdx.x;
+  const int wv = threadIdx.x / 64;
   const int lane = threadIdx.x % 64;
   const int Hq = a.num_q_heads;
   if (pair >= a.num_seqs * Hq) return;
@@ -497,7 +593,7 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(RowAttnArgs a) {
   const bool balanced = a.balance_pieces > 0;
   int ns, np = 0, first = 0;
   if (balanced) {
-    // written by the first piece of the sequence in the split pass
+    // written by the wave holding the sequence's first step in the split pass
     first = a.piece_meta[2 * b];
     ns = a.piece_meta[2 * b + 1];
   } else {
@@ -510,51 +606,84 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(RowAttnArgs a) {
   const int S = a.ws_stride;
   const float* ml = a.ws_ml;
   const float* wo = a.ws_o + lane * EPL;
-  // state of the i-th merged term: balanced pieces first .. first + ns - 1 of
-  // the sequence; else the pair's splits 0 .. ns-1, then its prefix chunks at
-  // num_splits ..
+  // state of the i-th merged term: parts first .. first + ns - 1 of the
+  // sequence (token-balanced); else the pair's splits 0 .. ns-1, then its
+  // prefix chunks at num_splits ..
   auto slot = [&](int i) -> int64_t {
     if (balanced) return (int64_t)(first + i) * Hq + h;
     return (int64_t)pair * S + (i < ns ? i : a.num_splits + (i - ns));
   };
-  // States are read kBatch at a time, so that their loads are in flight
-  // together (the first batch's with the maxima of the rest: one memory round
-  // trip for up to kBatch states); they are combined one by one in slot order.
-  constexpr int kBatch = 8;
   const int n = ns + np;
-  float mv[kBatch], lv[kBatch], ov[kBatch][EPL];
-  auto load_batch = [&](int i0) {
+  const int nw = min(kReduceWaves, (n + kBatch - 1) / kBatch);
+  const int per = (n + nw - 1) / nw;
+  const int lo = min(n, wv * per), hi = min(n, lo + per);
+
+  // This wave's slice [lo, hi): states read kBatch at a time, so that their
+  // loads are in flight together (the first batch's with the maxima of the
+  // rest: one memory round trip for up to kBatch states), combined one by one.
+  float M = kNegInf, den = 0.f, acc[EPL] = {};
+  if (lo < hi) {
+    float mv[kBatch], lv[kBatch], ov[kBatch][EPL];
+    auto load_batch = [&](int i0) {
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int64_t j = slot(min(i0 + k, n - 1));  // past the end: the last state again, unused
-      mv[k] = ml[2 * j];
-      lv[k] = ml[2 * j + 1];
+      for (int k = 0; k < kBatch; ++k) {
+        const int64_t j = slot(min(i0 + k, hi - 1));  // past the end: the last state again, unused
+        mv[k] = ml[2 * j];
+        lv[k] = ml[2 * j + 1];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) ov[k][e] = wo[j * D + e];
+        for (int e = 0; e < EPL; ++e) ov[k][e] = wo[j * D + e];
+      }
+    };
+    load_batch(lo);
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) M = fmaxf(M, mv[k]);  // repeats leave the max alone
+    for (int i0 = lo + kBatch; i0 < hi; i0 += kBatch) {
+      float mx[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) mx[k] = ml[2 * slot(min(i0 + k, hi - 1))];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) M = fmaxf(M, mx[k]);
     }
-  };
-  load_batch(0);
-  float M = kNegInf;
+    for (int i0 = lo; i0 < hi; i0 += kBatch) {
+      if (i0 > lo) load_batch(i0);
 #pragma unroll
-  for (int k = 0; k < kBatch; ++k) M = fmaxf(M, mv[k]);  // repeats leave the max alone
-  for (int i0 = kBatch; i0 < n; i0 += kBatch) {
-    float mx[kBatch];
+      for (int k = 0; k < kBatch; ++k) {
+        if (i0 + k >= hi) break;
+        const float w = exp2_hw(mv[k] - M);
+        den = fmaf(w, lv[k], den);
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) mx[k] = ml[2 * slot(min(i0 + k, n - 1))];
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) M = fmaxf(M, mx[k]);
+        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(w, ov[k][e], acc[e]);
+      }
+    }
   }
-  float den = 0.f, acc[EPL] = {};
-  for (int i0 = 0; i0 < n; i0 += kBatch) {
-    if (i0 > 0) load_batch(i0);
+  if (nw > 1) {
+    // merge the slices' (M, den, acc) in slice order (nw is the same for the
+    // whole workgroup, so every wave reaches the barrier)
+    __shared__ float part_m[kReduceWaves], part_l[kReduceWaves];
+    __shared__ float part_o[kReduceWaves][D];
+    if (wv < nw) {
+      if (lane == 0) {
+        part_m[wv] = M;
+        part_l[wv] = den;
+      }
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      if (i0 + k >= n) break;
-      const float w = exp2_hw(mv[k] - M);
-      den = fmaf(w, lv[k], den);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(w, ov[k][e], acc[e]);
+      for (int e = 0; e < EPL; ++e) part_o[wv][lane * EPL + e] = acc[e];
     }
+    __syncthreads();
+    if (wv != 0) return;
+    M = kNegInf;
+    for (int j = 0; j < nw; ++j) M = fmaxf(M, part_m[j]);
+    den = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+    for (int j = 0; j < nw; ++j) {
+      const float w = exp2_hw(part_m[j] - M);
+      den = fmaf(w, part_l[j], den);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(w, part_o[j][lane * EPL + e], acc[e]);
+    }
+  } else if (wv != 0) {
+    return;
   }
   const float inv = 1.0f / den;
   if constexpr (BF16) {

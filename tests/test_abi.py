@@ -74,13 +74,16 @@ def test_workspace_and_split_queries():
     L = pkv.lib()
     assert L.pkv_decode_workspace_bytes(4, 8, 128, 100, 128) == 0
     assert L.pkv_decode_workspace_bytes(4, 8, 128, 300, 128) == 4 * 8 * 3 * 130 * 4
-    for B, Hkv, maxL in [(256, 8, 1024), (64, 8, 8192), (200, 8, 32768), (4, 2, 100), (1, 1, 1)]:
-        s = L.pkv_decode_split_tokens(B, Hkv * 4, Hkv, 128, maxL, 256, 1)
-        assert (s > 0 and s % 64 == 0) or s == pkv.SPLIT_BALANCED
-    # token-balanced pieces: about 1024 pieces (at least one per sequence) of
-    # states, then two ints of piece bounds per sequence
-    assert L.pkv_decode_workspace_bytes(4, 8, 128, 100, pkv.SPLIT_BALANCED) == 1024 * 8 * 130 * 4 + 4 * 8
-    assert L.pkv_decode_workspace_bytes(1500, 4, 64, 9, pkv.SPLIT_BALANCED) == 1500 * 4 * 66 * 4 + 1500 * 8
+    # the library's choice: token-balanced ranges above 256 tokens of context,
+    # else one split per sequence (the context rounded up to 64)
+    for B, Hkv, maxL in [(256, 8, 1024), (64, 8, 8192), (200, 8, 32768), (4096, 8, 2048), (1, 1, 257)]:
+        assert L.pkv_decode_split_tokens(B, Hkv * 4, Hkv, 128, maxL, 256, 1) == pkv.SPLIT_BALANCED
+    for B, Hkv, maxL, split in [(4, 2, 100, 128), (1, 1, 1, 64), (4096, 8, 256, 256)]:
+        assert L.pkv_decode_split_tokens(B, Hkv * 4, Hkv, 128, maxL, 256, 1) == split
+    # token-balanced ranges: state slots for 1024 waves plus one per sequence
+    # (a wave's range can end inside a sequence), then two ints per sequence
+    assert L.pkv_decode_workspace_bytes(4, 8, 128, 100, pkv.SPLIT_BALANCED) == (1024 + 4) * 8 * 130 * 4 + 4 * 8
+    assert L.pkv_decode_workspace_bytes(1500, 4, 64, 9, pkv.SPLIT_BALANCED) == (1024 + 1500) * 4 * 66 * 4 + 1500 * 8
     # other negative splits are rejected before anything else is looked at
     assert _dec(L, maxL=1000, split=-2) == -1
 

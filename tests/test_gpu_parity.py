@@ -234,8 +234,8 @@ def test_config3_long_decode_splitk(dtype):
 @pytest.mark.parametrize("config", [2, 3])
 @pytest.mark.parametrize("dtype", [None, "f32"])
 def test_balanced_pieces_full_configs(config, dtype):
-    """Token-balanced pieces (about 1024 per launch, cut across the batch) on
-    the Qwen3-shaped and long-context decode workloads, every row."""
+    """Token-balanced ranges (1024 waves of equal step counts, cut across the
+    batch) on the Qwen3-shaped and long-context decode workloads, every row."""
     w = W.make_config(config, dtype=dtype)
     log(f"config {config} dtype={w.dtype} balanced pieces")
     step = DeviceStep(w)
@@ -247,8 +247,9 @@ def test_balanced_pieces_full_configs(config, dtype):
 
 
 def test_balanced_pieces_more_sequences_than_pieces():
-    """1100 sequences and about 1024 pieces: every sequence is one piece and
-    writes its output in the first pass; plus one long sequence, cut in many."""
+    """1100 short sequences and one long one over at most 1024 waves: most
+    waves' ranges cover several whole sequences (written in the first pass),
+    the long one is cut into many parts."""
     rng = np.random.default_rng(16)
     lens = [int(x) for x in rng.integers(1, 300, size=1100)] + [5000]
     w = _decode_case("f32", 8, 2, 64, 16, lens, seed=16)
@@ -258,6 +259,49 @@ def test_balanced_pieces_more_sequences_than_pieces():
     kc, vc = _check_store(step, w)
     err = max_abs(to_host(step.dec_out, "f32"), oracle_decode(w, kc, vc), "f32")
     assert err <= 1e-5, err
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_balanced_single_long_sequence(dtype):
+    """One 24000-token sequence cut into hundreds of parts (375 in bf16, 512 =
+    the most per sequence in f32), so the merge runs its eight-wave slice
+    path; f32 makes 1e-5 see a single lost part."""
+    w = _decode_case(dtype, 32, 8, 128, 16, [24000], seed=21)
+    log(f"balanced single long sequence {dtype}")
+    step = DeviceStep(w)
+    step.step(split_tokens=pkv.SPLIT_BALANCED)
+    kc, vc = _check_store(step, w)
+    err = max_abs(to_host(step.dec_out, w.dtype), oracle_decode(w, kc, vc), w.dtype)
+    log(f"balanced single long sequence max abs error {err:.3g}")
+    assert err <= tol(w.dtype), err
+
+
+def test_balanced_ranges_cross_sequences_with_empty_contexts():
+    """Ranges that end inside one sequence and start the next, with empty
+    contexts (zero rows) and a one-token context among them, and a step count
+    below 16 * 1024 (fewer waves than the cap)."""
+    rng = np.random.default_rng(22)
+    lens = [int(x) for x in rng.integers(1, 700, size=90)]
+    lens[7] = 1
+    w = _decode_case("f32", 16, 4, 64, 32, lens, seed=22)
+    log("balanced ranges across sequences, empty contexts")
+    step = DeviceStep(w)
+    step.store()
+    kc, vc = _check_store(step, w)
+    empty = (3, 40, 89)
+    cl_host = np.asarray(w.dec_context_lens, dtype=np.int32).copy()
+    cl_host[list(empty)] = 0
+    cl = torch.from_numpy(cl_host).cuda()
+    step.dec_out.fill_(1.0)
+    pkv.paged_decode_attn(step.dec_q, step.k_cache, step.v_cache, step.dec_bt, cl, w.scale, step.dec_out,
+                          max_context_len=int(cl_host.max()), split_tokens=pkv.SPLIT_BALANCED)
+    torch.cuda.synchronize()
+    got = to_host(step.dec_out, "f32")
+    rows = [b for b in range(len(lens)) if b not in empty]
+    err = max_abs(got[rows], oracle_decode(w, kc, vc, rows=rows), "f32")
+    assert err <= 1e-5, err
+    for b in empty:
+        assert not np.any(got[b]), f"row {b} of an empty context is not zero"
 
 
 # The prefix-cached prefill and mixed-step workloads are compared row by row in
