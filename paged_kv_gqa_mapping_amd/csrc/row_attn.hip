@@ -119,15 +119,29 @@ hipError_t launch_row_attn(const RowAttnArgs& a, int32_t dtype, int32_t head_dim
   return prefill ? dispatch<true>(a, dtype, head_dim, stream) : dispatch<false>(a, dtype, head_dim, stream);
 }
 
+// Pair count up to which the merge gives each (sequence, head) a workgroup.
+constexpr int64_t kReduceWidePairs = 1024;
+
+template <bool BF16, int D>
+void launch_reduce(const RowAttnArgs& a, bool wide, dim3 grid, dim3 block, hipStream_t stream) {
+  if (wide)
+    hipLaunchKernelGGL((decode_reduce_kernel<BF16, D, true>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_reduce_kernel<BF16, D, false>), grid, block, 0, stream, a);
+}
+
 hipError_t launch_decode_reduce(const RowAttnArgs& a, int32_t dtype, int32_t head_dim, hipStream_t stream) {
-  const int64_t pairs = (int64_t)a.num_seqs * a.num_q_heads;  // one workgroup each
+  const int64_t pairs = (int64_t)a.num_seqs * a.num_q_heads;
   if (pairs <= 0) return hipSuccess;
   if (pairs > 0x7fffffff) return hipErrorInvalidValue;
-  dim3 grid((unsigned)pairs), block(kReduceWaves * 64);
-  if (dtype == kBF16 && head_dim == 128) hipLaunchKernelGGL((decode_reduce_kernel<true, 128>), grid, block, 0, stream, a);
-  else if (dtype == kBF16 && head_dim == 64) hipLaunchKernelGGL((decode_reduce_kernel<true, 64>), grid, block, 0, stream, a);
-  else if (dtype == kF32 && head_dim == 128) hipLaunchKernelGGL((decode_reduce_kernel<false, 128>), grid, block, 0, stream, a);
-  else if (dtype == kF32 && head_dim == 64) hipLaunchKernelGGL((decode_reduce_kernel<false, 64>), grid, block, 0, stream, a);
+  // few pairs: a workgroup each, its waves sharing the pair's states; else a
+  // wave each (kReduceWaves pairs per workgroup)
+  const bool wide = pairs <= kReduceWidePairs;
+  dim3 grid((unsigned)(wide ? pairs : (pairs + kReduceWaves - 1) / kReduceWaves)), block(kReduceWaves * 64);
+  if (dtype == kBF16 && head_dim == 128) launch_reduce<true, 128>(a, wide, grid, block, stream);
+  else if (dtype == kBF16 && head_dim == 64) launch_reduce<true, 64>(a, wide, grid, block, stream);
+  else if (dtype == kF32 && head_dim == 128) launch_reduce<false, 128>(a, wide, grid, block, stream);
+  else if (dtype == kF32 && head_dim == 64) launch_reduce<false, 64>(a, wide, grid, block, stream);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -570,21 +570,94 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
   }
 }
 
+__device__ __forceinline__ float readlane_f(float x, int src) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), src));
+}
+
+// One wave merges states lo .. hi-1 of a pair (slot(i) gives their rows):
+// M = max_i m_i, den = sum_i 2^(m_i - M) l_i and acc = sum_i 2^(m_i - M) o_i,
+// the sums taken one state at a time in index order.  The maxima and sums are
+// read 64 states per load (lane k holding state c + k); the partial outputs
+// kOB states at a time, the first batch requested together with the first
+// maxima, so that up to min(64, kOB) states cost one memory round trip.
+template <int D, int kOB, typename Slot>
+__device__ __forceinline__ void merge_states(int lo, int hi, const Slot& slot, const float* ml, const float* wo,
+                                             int lane, float& M, float& den, float (&acc)[D / 64]) {
+  constexpr int EPL = D / 64;
+  static_assert(64 % kOB == 0, "output batches must not straddle a 64-state chunk");
+  M = kNegInf;
+  den = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  if (lo >= hi) return;
+  float ov[kOB][EPL];
+  auto load_o = [&](int i0) {
+#pragma unroll
+    for (int k = 0; k < kOB; ++k) {
+      if (i0 + k < hi) {  // (uniform) states past the end are not read, nor used
+        const int64_t j = slot(i0 + k);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) ov[k][e] = wo[j * D + e];
+      }
+    }
+  };
+  load_o(lo);
+  auto load_ml = [&](int c, float& m, float& l) {
+    const int i = c + lane;
+    m = kNegInf;  // lanes past the end: weight 2^-inf = 0, never read
+    l = 0.f;
+    if (i < hi) {
+      const int64_t j = slot(i);
+      m = ml[2 * j];
+      l = ml[2 * j + 1];
+    }
+  };
+  float m0, l0;
+  load_ml(lo, m0, l0);
+  float mx = m0;
+  for (int c = lo + 64; c < hi; c += 64) {
+    const int i = c + lane;
+    if (i < hi) mx = fmaxf(mx, ml[2 * slot(i)]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  M = mx;
+  for (int c = lo; c < hi; c += 64) {
+    float mc = m0, lc = l0;
+    if (c > lo) load_ml(c, mc, lc);
+    const float wc = exp2_hw(mc - M);
+    const int cend = min(hi, c + 64);
+    for (int i0 = c; i0 < cend; i0 += kOB) {
+      if (i0 > lo) load_o(i0);
+#pragma unroll
+      for (int k = 0; k < kOB; ++k) {
+        if (i0 + k >= cend) break;
+        const float w = readlane_f(wc, i0 + k - c);
+        den = fmaf(w, readlane_f(lc, i0 + k - c), den);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(w, ov[k][e], acc[e]);
+      }
+    }
+  }
+}
+
 // Merge the split states of each (sequence, query head): M = max_j m_j,
 // w_j = 2^(m_j - M), out = sum_j w_j o_j / sum_j w_j l_j, over the pair's
 // states in slot order: its splits (or token-balanced parts), then the group
-// pass's chunks of its shared prefix (if any).  One workgroup per pair; its
-// n states are cut into nw = min(kReduceWaves, ceil(n / 8)) consecutive
-// slices, one per wave, and each wave merges its slice as above (reading the
-// states eight at a time, combining them one by one); with nw > 1 the slice
-// results are then merged the same way, in slice order.
+// pass's chunks of its shared prefix (if any).
+//  * WIDE = false (many pairs): one wave per pair (merge_states over all of
+//    its states), kReduceWaves pairs per workgroup.
+//  * WIDE = true (few pairs, so each may hold hundreds of states): one
+//    workgroup per pair; its n states are cut into nw = min(kReduceWaves,
+//    ceil(n / 8)) consecutive slices, one per wave, and with nw > 1 the
+//    slice results are merged the same way, in slice order.
+// With nw = 1 both give the same bits.
 constexpr int kReduceWaves = 8;
-template <bool BF16, int D>
+template <bool BF16, int D, bool WIDE>
 __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce_kernel(RowAttnArgs a) {
   constexpr int EPL = D / 64;  // elements per lane
-  constexpr int kBatch = 8;
-  const int pair = blockIdx.x;
-  const int wv = threadIdx.x / 64;
+  const int pair = WIDE ? blockIdx.x : blockIdx.x * kReduceWaves + threadIdx.x / 64;
+  const int wv = WIDE ? threadIdx.x / 64 : 0;
   const int lane = threadIdx.x % 64;
   const int Hq = a.num_q_heads;
   if (pair >= a.num_seqs * Hq) return;
@@ -604,8 +677,6 @@ __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce_kernel(RowAtt
   }
   if (np == 0 && ns <= 1) return;
   const int S = a.ws_stride;
-  const float* ml = a.ws_ml;
-  const float* wo = a.ws_o + lane * EPL;
   // state of the i-th merged term: parts first .. first + ns - 1 of the
   // sequence (token-balanced); else the pair's splits 0 .. ns-1, then its
   // prefix chunks at num_splits ..
@@ -614,49 +685,12 @@ __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce_kernel(RowAtt
     return (int64_t)pair * S + (i < ns ? i : a.num_splits + (i - ns));
   };
   const int n = ns + np;
-  const int nw = min(kReduceWaves, (n + kBatch - 1) / kBatch);
+  const int nw = WIDE ? min(kReduceWaves, (n + 7) / 8) : 1;
   const int per = (n + nw - 1) / nw;
   const int lo = min(n, wv * per), hi = min(n, lo + per);
-
-  // This wave's slice [lo, hi): states read kBatch at a time, so that their
-  // loads are in flight together (the first batch's with the maxima of the
-  // rest: one memory round trip for up to kBatch states), combined one by one.
-  float M = kNegInf, den = 0.f, acc[EPL] = {};
-  if (lo < hi) {
-    float mv[kBatch], lv[kBatch], ov[kBatch][EPL];
-    auto load_batch = [&](int i0) {
-#pragma unroll
-      for (int k = 0; k < kBatch; ++k) {
-        const int64_t j = slot(min(i0 + k, hi - 1));  // past the end: the last state again, unused
-        mv[k] = ml[2 * j];
-        lv[k] = ml[2 * j + 1];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) ov[k][e] = wo[j * D + e];
-      }
-    };
-    load_batch(lo);
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) M = fmaxf(M, mv[k]);  // repeats leave the max alone
-    for (int i0 = lo + kBatch; i0 < hi; i0 += kBatch) {
-      float mx[kBatch];
-#pragma unroll
-      for (int k = 0; k < kBatch; ++k) mx[k] = ml[2 * slot(min(i0 + k, hi - 1))];
-#pragma unroll
-      for (int k = 0; k < kBatch; ++k) M = fmaxf(M, mx[k]);
-    }
-    for (int i0 = lo; i0 < hi; i0 += kBatch) {
-      if (i0 > lo) load_batch(i0);
-#pragma unroll
-      for (int k = 0; k < kBatch; ++k) {
-        if (i0 + k >= hi) break;
-        const float w = exp2_hw(mv[k] - M);
-        den = fmaf(w, lv[k], den);
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(w, ov[k][e], acc[e]);
-      }
-    }
-  }
-  if (nw > 1) {
+  float M, den, acc[EPL];
+  merge_states<D, 16>(lo, hi, slot, a.ws_ml, a.ws_o + lane * EPL, lane, M, den, acc);
+  if (WIDE && nw > 1) {
     // merge the slices' (M, den, acc) in slice order (nw is the same for the
     // whole workgroup, so every wave reaches the barrier)
     __shared__ float part_m[kReduceWaves], part_l[kReduceWaves];
