@@ -288,8 +288,12 @@ int pkv_paged_decode_store_attn(const void* q, const void* k, const void* v, voi
  *   max_own_len    >= every context_lens[b] - shared_lens[b] (the keys a
  *                  sequence attends on its own); it sizes the split pass.
  *                  0 means max_context_len.
- *   split_tokens   split length of the split pass, or 0 for the library's
- *                  choice for max_own_len.
+ *   split_tokens   split length of the split pass, PKV_SPLIT_BALANCED (the
+ *                  own keys of the batch in token-balanced ranges, as in
+ *                  pkv_paged_decode_attn), or 0 for the library's choice:
+ *                  token-balanced ranges when num_seqs * max_own_len is at
+ *                  least 1024 * 256 and max_own_len > 256, else splits down to
+ *                  64 keys aiming at about 2048 waves.
  *   workspace      at least pkv_cascade_workspace_bytes(...) bytes (same
  *                  sizes and split_tokens as the call).
  * With num_groups == 0 or max_shared_len == 0 this is pkv_paged_decode_attn

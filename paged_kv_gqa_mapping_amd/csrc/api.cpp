@@ -94,11 +94,15 @@ int32_t auto_split(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_l
 #define PKV_BALANCE_PIECES 1024
 #endif
 constexpr int32_t kBalancePieces = PKV_BALANCE_PIECES;
-// states [W + B, Hq, D] and [W + B, Hq, 2] floats (slot w + b for the part of
-// sequence b in wave w's range), then [B, 2] ints (first slot, count)
-int64_t balanced_state_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim) {
+// State rows [W + B, Hq] (slot w + b for the part of sequence b in wave w's
+// range), then with shared prefixes [B, Hq, C] for the group pass's chunks;
+// D floats each in ws_o and 2 in ws_ml, then [B, 2] ints (first slot, count).
+int64_t balanced_rows(int32_t num_seqs, int32_t num_q_heads, int32_t prefix_states) {
+  return ((int64_t)kBalancePieces + num_seqs) * num_q_heads + (int64_t)num_seqs * num_q_heads * prefix_states;
+}
+int64_t balanced_state_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t prefix_states = 0) {
   if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0) return 0;
-  return ((int64_t)kBalancePieces + num_seqs) * num_q_heads * (head_dim + 2) * (int64_t)sizeof(float) +
+  return balanced_rows(num_seqs, num_q_heads, prefix_states) * (head_dim + 2) * (int64_t)sizeof(float) +
          (int64_t)num_seqs * 2 * (int64_t)sizeof(int32_t);
 }
 // The library's choice for split_tokens = 0: token-balanced ranges for any
@@ -123,6 +127,7 @@ struct DecodePlan {
   int32_t S = 1;      // split states per pair (grid splits)
   int32_t chunk = 0;  // keys per group-pass state
   int32_t C = 0;      // group-pass states per pair
+  bool balanced = false;  // own keys in token-balanced ranges instead of splits
 };
 
 // Shared-prefix plan.  The split pass only covers each sequence's own keys,
@@ -136,7 +141,16 @@ DecodePlan cascade_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_he
   DecodePlan p;
   const int32_t own = (max_own_len > 0 && max_own_len < max_context_len) ? max_own_len : max_context_len;
   p.split = split_tokens;
-  if (!p.split) {
+  // token-balanced ranges when asked for, or when the own keys could give each
+  // of the kBalancePieces waves 256 of them; fewer own keys keep the fine
+  // splits below, which run more (shorter) waves
+  p.balanced = split_tokens == PKV_SPLIT_BALANCED ||
+               (split_tokens == 0 && own > 256 &&
+                (int64_t)std::max(num_seqs, 1) * own >= (int64_t)kBalancePieces * 256);
+  if (p.balanced) {
+    p.split = 0;
+    p.S = kBalancePieces;
+  } else if (!p.split) {
     // Own keys are often few (a short suffix behind a long shared prompt), and the
     // plain rule's 256/512-token floor would then leave a small grid of long
     // waves; splits down to 64 keys keep about 2048 waves in flight.  Long own
@@ -146,7 +160,7 @@ DecodePlan cascade_plan(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_he
     while (fine < own && base * ((own + fine - 1) / fine) > 2048) fine *= 2;
     p.split = std::min(fine, auto_split(std::max(num_seqs, 1), std::max(num_kv_heads, 1), own));
   }
-  p.S = std::max(1, (own + p.split - 1) / p.split);
+  if (!p.balanced) p.S = std::max(1, (own + p.split - 1) / p.split);
   if (num_groups > 0 && max_shared_len > 0) {
     // chunks of the shared prefix: from 256 keys, doubled while the group pass
     // would have more workgroups than the 256 CUs hold at once (one each: the
@@ -196,15 +210,16 @@ int prepare_decode(DecodeCall& call, const void* q, const void* k_cache, const v
   if (split_tokens != PKV_SPLIT_BALANCED && (split_tokens < 0 || split_tokens % 64))
     return fail(PKV_ERR_INVALID_ARG, "split_tokens %d is not 0, PKV_SPLIT_BALANCED or a positive multiple of 64",
                 split_tokens);
-  const bool balanced = !plan && (split_tokens == PKV_SPLIT_BALANCED ||
-                                  (split_tokens == 0 && auto_balanced(num_seqs, num_kv_heads, max_context_len)));
+  const bool balanced = plan ? plan->balanced
+                             : (split_tokens == PKV_SPLIT_BALANCED ||
+                                (split_tokens == 0 && auto_balanced(num_seqs, num_kv_heads, max_context_len)));
   const int32_t split = balanced ? 0
                         : plan   ? plan->split
                         : split_tokens ? split_tokens
                                        : auto_split(num_seqs, num_kv_heads, max_context_len);
   const int32_t S = balanced ? kBalancePieces : plan ? plan->S : std::max(1, (max_context_len + split - 1) / split);
   const int32_t prefix_states = plan ? plan->C : 0;
-  const int64_t need = balanced ? balanced_state_bytes(num_seqs, num_q_heads, head_dim)
+  const int64_t need = balanced ? balanced_state_bytes(num_seqs, num_q_heads, head_dim, prefix_states)
                                 : state_bytes(num_seqs, num_q_heads, head_dim, S, prefix_states);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(PKV_ERR_WORKSPACE, "decode workspace of %lld bytes needed, %lld given%s", (long long)need,
@@ -223,12 +238,14 @@ int prepare_decode(DecodeCall& call, const void* q, const void* k_cache, const v
   a.context_lens = context_lens;
   a.out = out;
   a.ws_o = need > 0 ? static_cast<float*>(workspace) : nullptr;
-  const int64_t state_rows =
-      balanced ? ((int64_t)S + num_seqs) * num_q_heads : (int64_t)num_seqs * num_q_heads * (S + prefix_states);
+  const int64_t state_rows = balanced ? balanced_rows(num_seqs, num_q_heads, prefix_states)
+                                      : (int64_t)num_seqs * num_q_heads * (S + prefix_states);
   a.ws_ml = need > 0 ? a.ws_o + state_rows * head_dim : nullptr;
   if (balanced) {
     a.balance_pieces = S;
     a.piece_meta = reinterpret_cast<int32_t*>(a.ws_ml + state_rows * 2);
+    a.prefix_slot0 = ((int64_t)S + num_seqs) * num_q_heads;
+    a.prefix_states = prefix_states;
   }
   a.scale_log2 = scale * 1.4426950408889634f;
   a.num_seqs = num_seqs;
@@ -341,14 +358,16 @@ int64_t pkv_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_
 int64_t pkv_cascade_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                     int32_t max_context_len, int32_t max_own_len, int32_t split_tokens,
                                     int32_t num_groups, int32_t max_group_size, int32_t max_shared_len) {
-  if (max_context_len <= 0 || split_tokens < 0 || max_shared_len < 0 || num_groups < 0 || num_q_heads <= 0 ||
+  if (max_context_len <= 0 || (split_tokens < 0 && split_tokens != PKV_SPLIT_BALANCED) || max_shared_len < 0 ||
+      num_groups < 0 || num_q_heads <= 0 ||
       num_kv_heads <= 0 || num_q_heads % num_kv_heads)
     return 0;
   const bool cascade = num_groups > 0 && max_shared_len > 0;
   const DecodePlan p = cascade_plan(num_seqs, num_q_heads, num_kv_heads, max_context_len,
                                     cascade ? max_own_len : 0, split_tokens, cascade ? num_groups : 0,
                                     max_group_size, cascade ? max_shared_len : 0);
-  return state_bytes(num_seqs, num_q_heads, head_dim, p.S, p.C);
+  return p.balanced ? balanced_state_bytes(num_seqs, num_q_heads, head_dim, p.C)
+                    : state_bytes(num_seqs, num_q_heads, head_dim, p.S, p.C);
 }
 
 #define PKV_DECODE_ARGS                                                                                        \
@@ -515,8 +534,9 @@ int pkv_cascade_decode_attn(const void* q, const void* k_cache, const void* v_ca
     if (!(scale > 0.f) || !std::isfinite(scale))
       return fail(PKV_ERR_INVALID_ARG, "shared-prefix decode needs a finite scale > 0 (got %g)", (double)scale);
   }
-  if (split_tokens < 0 || split_tokens % 64)
-    return fail(PKV_ERR_INVALID_ARG, "split_tokens %d is not 0 or a positive multiple of 64", split_tokens);
+  if (split_tokens != PKV_SPLIT_BALANCED && (split_tokens < 0 || split_tokens % 64))
+    return fail(PKV_ERR_INVALID_ARG, "split_tokens %d is not 0, PKV_SPLIT_BALANCED or a positive multiple of 64",
+                split_tokens);
   int st = check_heads(num_q_heads, num_kv_heads);
   if (st) return st;
   const DecodePlan plan = cascade_plan(num_seqs, num_q_heads, num_kv_heads, std::max(max_context_len, 1),
@@ -544,10 +564,18 @@ int pkv_cascade_decode_attn(const void* q, const void* k_cache, const void* v_ca
     g.group_offsets = group_offsets;
     g.group_seqs = group_seqs;
     g.shared_lens = shared_lens;
-    g.ws_o = r.ws_o;
-    g.ws_ml = r.ws_ml;
-    g.ws_stride = r.ws_stride;
-    g.slot0 = r.num_splits;
+    if (r.balance_pieces > 0) {
+      // the chunk states' own region: pair p's chunk c at row p * C + c of it
+      g.ws_o = r.ws_o + r.prefix_slot0 * head_dim;
+      g.ws_ml = r.ws_ml + r.prefix_slot0 * 2;
+      g.ws_stride = plan.C;
+      g.slot0 = 0;
+    } else {
+      g.ws_o = r.ws_o;
+      g.ws_ml = r.ws_ml;
+      g.ws_stride = r.ws_stride;
+      g.slot0 = r.num_splits;
+    }
     g.chunk_tokens = plan.chunk;
     g.num_groups = num_groups;
     g.num_chunks = plan.C;

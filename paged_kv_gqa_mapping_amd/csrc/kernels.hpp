@@ -57,8 +57,13 @@ struct RowAttnArgs {
   // ([w + b, Hq] of ws_o / ws_ml; a sequence's parts have consecutive slots),
   // and the wave holding b's first step writes (first slot, part count) to
   // piece_meta[b].
+  // With shared prefixes (kv_start set) each sequence's steps count only its
+  // own keys [kv_start[b], L_b), and the group pass's chunk states of pair p
+  // sit at rows prefix_slot0 + p * prefix_states + chunk.
   int32_t balance_pieces;
   int32_t* piece_meta;  // [B, 2]
+  int64_t prefix_slot0;
+  int32_t prefix_states;
 };
 
 // Picks the instantiation (dtype, head_dim, KV heads per wave, group size) and launches.

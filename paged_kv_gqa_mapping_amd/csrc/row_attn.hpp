@@ -129,6 +129,7 @@ __device__ __forceinline__ long long wave_inclusive_scan_i64(long long x, int la
 constexpr int kScanBatch = 4;
 struct StepScan {
   int L[kScanBatch];        // context lengths of sequences lane + 64 k
+  int st[kScanBatch];       // their first own key (kv_start, else 0)
   long long n[kScanBatch];  // their steps (0 past the end)
 };
 __device__ __forceinline__ void scan_load(const RowAttnArgs& a, int U, int i0, int lane, StepScan& sc) {
@@ -136,9 +137,11 @@ __device__ __forceinline__ void scan_load(const RowAttnArgs& a, int U, int i0, i
   for (int k = 0; k < kScanBatch; ++k) {
     const int i = i0 + 64 * k + lane;
     sc.L[k] = i < a.num_seqs ? max(a.context_lens[i], 0) : 0;
+    sc.st[k] = (i < a.num_seqs && a.kv_start) ? a.kv_start[i] : 0;
   }
 #pragma unroll
-  for (int k = 0; k < kScanBatch; ++k) sc.n[k] = i0 + 64 * k + lane < a.num_seqs ? steps_of(sc.L[k], U) : 0;
+  for (int k = 0; k < kScanBatch; ++k)
+    sc.n[k] = i0 + 64 * k + lane < a.num_seqs ? steps_of(sc.L[k] - sc.st[k], U) : 0;
 }
 // N, and the most steps of any one sequence in nmax.
 __device__ __forceinline__ long long total_steps(const RowAttnArgs& a, int U, int lane, StepScan& first,
@@ -177,7 +180,8 @@ __device__ __forceinline__ int balanced_waves(int W, long long N, long long nmax
   return (int)min(w, N);
 }
 __device__ __forceinline__ bool sequence_of_step(const RowAttnArgs& a, int U, long long s, int lane,
-                                                 const StepScan& first, int& b, long long& base, int& L) {
+                                                 const StepScan& first, int& b, long long& base, int& L,
+                                                 int& start) {
   long long run = 0;
   StepScan sc = first;
   for (int i0 = 0; i0 < a.num_seqs; i0 += 64 * kScanBatch) {
@@ -193,6 +197,7 @@ __device__ __forceinline__ bool sequence_of_step(const RowAttnArgs& a, int U, lo
         b = i0 + 64 * k + src;
         base = readlane_i64(off, src);
         L = __builtin_amdgcn_readlane(sc.L[k], src);
+        start = __builtin_amdgcn_readlane(sc.st[k], src);
         return true;
       }
       run += readlane_i64(incl, 63);
@@ -528,12 +533,16 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
     const int W = balanced_waves(a.balance_pieces, N, nmax);
     if (w >= W) return;
     const long long s_lo = (long long)w * N / W, s_hi = (long long)(w + 1) * N / W;
-    int b, L;
+    int b, L, start;
     long long base;
-    if (!sequence_of_step(a, U, s_lo, lane, first, b, base, L)) return;
+    if (!sequence_of_step(a, U, s_lo, lane, first, b, base, L, start)) return;
     for (long long s = s_lo; s < s_hi && b < a.num_seqs; ++b) {
-      if (s > s_lo) L = max(a.context_lens[b], 0);
-      const long long n = steps_of(L, U);
+      if (s > s_lo) {
+        L = max(a.context_lens[b], 0);
+        start = a.kv_start ? a.kv_start[b] : 0;
+      }
+      // own keys [start, L): keys below start belong to the group pass
+      const long long n = steps_of(L - start, U);
       const long long e = min(s_hi, base + n);
       const int w0 = wave_of_step(base, N, W);
       const int nst = wave_of_step(base + n - 1, N, W) - w0 + 1;
@@ -544,8 +553,9 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
       if (L == 0) {
         write_zeros(b);
       } else {
-        segment(b, b, (int)((s - base) * U), (int)min((long long)L, (e - base) * U), 0, L, nst,
-                (int64_t)(w + b) * Hq, 1);
+        // one part and no shared prefix: the output itself; else a state
+        segment(b, b, start + (int)((s - base) * U), (int)min((long long)L, start + (e - base) * U), 0, L,
+                start > 0 ? 0 : nst, (int64_t)(w + b) * Hq, 1);
       }
       s = e;
       base += n;
@@ -669,6 +679,8 @@ __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce_kernel(RowAtt
     // written by the wave holding the sequence's first step in the split pass
     first = a.piece_meta[2 * b];
     ns = a.piece_meta[2 * b + 1];
+    const int start = a.kv_start ? a.kv_start[b] : 0;
+    np = start > 0 ? (start + a.prefix_chunk - 1) / a.prefix_chunk : 0;
   } else {
     const int L = a.context_lens[b];
     const int start = a.kv_start ? a.kv_start[b] : 0;
@@ -678,10 +690,11 @@ __global__ __launch_bounds__(kReduceWaves * 64) void decode_reduce_kernel(RowAtt
   if (np == 0 && ns <= 1) return;
   const int S = a.ws_stride;
   // state of the i-th merged term: parts first .. first + ns - 1 of the
-  // sequence (token-balanced); else the pair's splits 0 .. ns-1, then its
-  // prefix chunks at num_splits ..
+  // sequence (token-balanced), then its prefix chunks in their own region;
+  // else the pair's splits 0 .. ns-1, then its prefix chunks at num_splits ..
   auto slot = [&](int i) -> int64_t {
-    if (balanced) return (int64_t)(first + i) * Hq + h;
+    if (balanced)
+      return i < ns ? (int64_t)(first + i) * Hq + h : a.prefix_slot0 + (int64_t)pair * a.prefix_states + (i - ns);
     return (int64_t)pair * S + (i < ns ? i : a.num_splits + (i - ns));
   };
   const int n = ns + np;

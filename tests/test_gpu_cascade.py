@@ -52,7 +52,7 @@ SHAPES = [(32, 8, 128, 16), (16, 8, 128, 256), (8, 1, 128, 32), (16, 2, 64, 8), 
           (16, 4, 64, 32)]
 
 
-@pytest.mark.parametrize("split", [0, 64])
+@pytest.mark.parametrize("split", [0, 64, pkv.SPLIT_BALANCED])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "-".join(map(str, s)))
 def test_cascade_sweep(shape, split):
     hq, hkv, d, bs = shape
