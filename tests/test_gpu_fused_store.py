@@ -39,7 +39,7 @@ def _same(x, y):
         assert np.array_equal(bits(p), bits(q))
 
 
-@pytest.mark.parametrize("split", [0, 64])
+@pytest.mark.parametrize("split", [0, 64, pkv.SPLIT_BALANCED])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "-".join(map(str, s)))
 def test_fused_store_matches_two_calls_bitwise(shape, split):
     dtype, hq, hkv, d, bs = shape

@@ -14,10 +14,9 @@ from gpu_harness import DeviceStep, log, to_dev, to_host
 pytestmark = pytest.mark.gpu
 
 
-def _capture_inputs(w):
+def _capture_inputs(w, split):
     st = DeviceStep(w)
     B, Hq, D = st.dec_q.shape
-    split = 256
     ws = torch.empty(max(pkv.decode_workspace_bytes(B, Hq, D, w.max_context_len, split), 16), dtype=torch.uint8,
                      device="cuda")
     k0, v0 = st.k_cache.clone(), st.v_cache.clone()
@@ -32,11 +31,12 @@ def _capture_inputs(w):
     return st, step, k0, v0
 
 
-def test_graph_replays_match_eager_bitwise():
+@pytest.mark.parametrize("split", [256, pkv.SPLIT_BALANCED])
+def test_graph_replays_match_eager_bitwise(split):
     seqs = [W.SeqSpec("prefill", 900, 300), W.SeqSpec("prefill", 130, 130)]
     seqs += [W.SeqSpec("decode", L, 1) for L in (1, 40, 700, 1500, 3000)]
     w = W.build("graph-step", 21, "bf16", 32, 8, 128, 64, seqs)
-    st, step, k0, v0 = _capture_inputs(w)
+    st, step, k0, v0 = _capture_inputs(w, split)
     log("eager step")
     step()
     torch.cuda.synchronize()
@@ -101,25 +101,26 @@ def test_graph_replay_sees_new_inputs():
         assert np.array_equal(got, to_host(out, "bf16"))
 
 
-def test_graph_fused_store_decode_step_matches_eager():
+@pytest.mark.parametrize("split", [512, pkv.SPLIT_BALANCED])
+def test_graph_fused_store_decode_step_matches_eager(split):
     """The decode step with the cache write fused in (one launch plus the merge)
     captured and replayed: outputs and caches equal the eager two-call step."""
     seqs = [W.SeqSpec("decode", L, 1) for L in (1, 17, 256, 257, 1000, 4000)]
     w = W.build("graph-fused", 23, "bf16", 32, 8, 128, 16, seqs)
     ref = DeviceStep(w)
     ref.store()
-    ref.decode(split_tokens=512)
+    ref.decode(split_tokens=split)
     torch.cuda.synchronize()
     st = DeviceStep(w)
     B, Hq, D = st.dec_q.shape
-    ws = torch.empty(max(pkv.decode_workspace_bytes(B, Hq, D, w.max_context_len, 512), 16), dtype=torch.uint8,
+    ws = torch.empty(max(pkv.decode_workspace_bytes(B, Hq, D, w.max_context_len, split), 16), dtype=torch.uint8,
                      device="cuda")
     k0, v0 = st.k_cache.clone(), st.v_cache.clone()
     out = torch.empty_like(st.dec_q)
 
     def step():
         pkv.paged_decode_store_attn(st.dec_q, st.new_k, st.new_v, st.k_cache, st.v_cache, st.dec_bt, st.dec_cl,
-                                    w.scale, out, max_context_len=w.max_context_len, split_tokens=512, workspace=ws)
+                                    w.scale, out, max_context_len=w.max_context_len, split_tokens=split, workspace=ws)
 
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
