@@ -1,9 +1,11 @@
 // Row attention on the vector units: one wave = one query row of every head
 // of HPW KV heads, streaming that row's keys through the block table.
 //
-//  * Decode: a row is sequence b's new token; its context is cut into splits
-//    of split_tokens keys, one wave per (sequence, KV-head group, split).
-//    Splits write an unnormalised softmax state that decode_reduce merges.
+//  * Decode: a row is sequence b's new token.  Its context is cut into splits
+//    of split_tokens keys, one wave per (sequence, KV-head group, split), or
+//    (token-balanced) the batch's contexts are cut into equal ranges that may
+//    cross sequences, one wave per (range, KV-head group).  A part of a
+//    context writes an unnormalised softmax state that decode_reduce merges.
 //  * Prefill rows (fp32 path): query i of sequence b attends keys 0..p with
 //    p = Lk - Lq + i, in one split.
 //
@@ -97,13 +99,14 @@ __device__ __forceinline__ long long wave_sum_i64(long long x) {
 }
 
 // Token-balanced decode (see RowAttnArgs): sequence b is n_b = max(1,
-// ceil(L_b / U)) steps of U tokens (an empty context counts one step, which
-// writes its row of zeros); the batch's N steps, sequence after sequence, are
-// cut into W <= N ranges of equal size (none empty), wave w taking
-// [floor(w N / W), floor((w + 1) N / W)).  A range may cross sequences: each (wave, sequence)
-// pair it touches is a segment, whose state goes to slot w + b.  Along the
-// step order w + b grows by at least one per segment, so the segments of one
-// sequence sit in consecutive slots, all below W + B.
+// ceil((L_b - kv_start_b) / U)) steps of U tokens over its own keys (an empty
+// context counts one step, which writes its row of zeros); the batch's N
+// steps, sequence after sequence, are cut into W <= N ranges of equal size
+// (none empty), wave w taking [floor(w N / W), floor((w + 1) N / W)).  A range
+// may cross sequences: each (wave, sequence) pair it touches is a segment,
+// whose state goes to slot w + b.  Along the step order w + b grows by at
+// least one per segment, so the segments of one sequence sit in consecutive
+// slots, all below W + B.
 __device__ __forceinline__ long long steps_of(int L, int U) { return max(1, (max(L, 0) + U - 1) / U); }
 // the wave whose range holds step x, 0 <= x < N
 __device__ __forceinline__ int wave_of_step(long long x, long long N, int W) {
