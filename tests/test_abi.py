@@ -176,6 +176,16 @@ def test_cascade_workspace_bytes():
     # twice the members: 2 member tiles x 8 head groups, so 1024-key chunks -> 16 chunks
     assert L.pkv_cascade_workspace_bytes(128, 32, 8, 128, 16896, 512, 256, 1, 128, 16384) == \
         128 * 32 * (2 + 16) * (128 + 2) * 4
+    # token-balanced own keys (asked for): slots for 1024 waves plus one per
+    # sequence, then the group-pass chunks in a region of their own, then two
+    # ints per sequence
+    assert L.pkv_cascade_workspace_bytes(64, 32, 8, 128, 16896, 512, pkv.SPLIT_BALANCED, 1, 64, 16384) == \
+        ((1024 + 64) * 32 + 64 * 32 * 32) * (128 + 2) * 4 + 64 * 8
+    # the library's choice: balanced when the own keys could give 1024 waves 256
+    # each (200 x 28,672 here; the 64 x 512 above keep the 256-key split)
+    ws = L.pkv_cascade_workspace_bytes(200, 32, 8, 128, 32768, 28672, 0, 1, 50, 4096)
+    assert ws == L.pkv_cascade_workspace_bytes(200, 32, 8, 128, 32768, 28672, pkv.SPLIT_BALANCED, 1, 50, 4096)
+    assert ws % 4 == 0 and ws > (1024 + 200) * 32 * 130 * 4
 
 
 @needs_lib
