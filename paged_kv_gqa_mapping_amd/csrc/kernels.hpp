@@ -50,9 +50,9 @@ struct RowAttnArgs {
   int32_t max_rows;      // prefill: max_seqlen_q
   // Token-balanced decode (balance_pieces = W > 0 instead of fixed splits):
   // sequence b is n_b = max(1, ceil(L_b / U)) steps of U tokens; the N steps
-  // of the batch, sequence after sequence, are cut into min(W, N) equal
-  // ranges, wave w (per KV-head group) taking steps [floor(w N / W'),
-  // floor((w + 1) N / W')), W' = min(W, N).
+  // of the batch, sequence after sequence, are cut into W' <= W ranges (the
+  // launch's waves per KV-head group), nearly equal (row_attn.hpp: the
+  // waves on odd-numbered dies take 1/16 less).
   // The part of sequence b in wave w's range writes its states at slot w + b
   // ([w + b, Hq] of ws_o / ws_ml; a sequence's parts have consecutive slots),
   // and the wave holding b's first step writes (first slot, part count) to

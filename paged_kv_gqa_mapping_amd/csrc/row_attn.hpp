@@ -101,16 +101,33 @@ __device__ __forceinline__ long long wave_sum_i64(long long x) {
 // Token-balanced decode (see RowAttnArgs): sequence b is n_b = max(1,
 // ceil((L_b - kv_start_b) / U)) steps of U tokens over its own keys (an empty
 // context counts one step, which writes its row of zeros); the batch's N
-// steps, sequence after sequence, are cut into W <= N ranges of equal size
-// (none empty), wave w taking [floor(w N / W), floor((w + 1) N / W)).  A range
-// may cross sequences: each (wave, sequence) pair it touches is a segment,
-// whose state goes to slot w + b.  Along the step order w + b grows by at
-// least one per segment, so the segments of one sequence sit in consecutive
-// slots, all below W + B.
+// steps, sequence after sequence, are cut into W <= N ranges (none empty),
+// wave w taking [start(w), start(w + 1)).  A range may cross sequences: each
+// (wave, sequence) pair it touches is a segment, whose state goes to slot
+// w + b.  Along the step order w + b grows by at least one per segment, so
+// the segments of one sequence sit in consecutive slots, all below W + B.
+//
+// The ranges are not quite equal.  Workgroup w runs on die w % 8 (the
+// dispatcher deals workgroups to the 8 dies in turn), and per-wave timestamps
+// show the waves of the odd-numbered dies streaming 5-11 % slower than those
+// of the even-numbered ones on every box measured; so the waves of odd w get
+// 1/16 less than the mean range and those of even w 1/16 more:
+// start(w) = floor(N (64 w + kOddDieShare (w mod 2)) / (64 W)).  (Where the
+// dies run alike, this costs at most 1/16 of the launch.)
+constexpr long long kOddDieShare = 4;  // in 64ths of a mean range
 __device__ __forceinline__ long long steps_of(int L, int U) { return max(1, (max(L, 0) + U - 1) / U); }
-// the wave whose range holds step x, 0 <= x < N
+// first step of wave w's range (N for w = W)
+__device__ __forceinline__ long long range_start(int w, long long N, int W) {
+  if (w >= W) return N;
+  return N * (64LL * w + kOddDieShare * (w & 1)) / (64LL * W);
+}
+// the wave whose range holds step x, 0 <= x < N: the equal split's wave, moved
+// by at most one (the ranges differ from the equal split's by under one range)
 __device__ __forceinline__ int wave_of_step(long long x, long long N, int W) {
-  return (int)(((x + 1) * (long long)W - 1) / N);
+  int w = (int)(((x + 1) * (long long)W - 1) / N);
+  while (w > 0 && range_start(w, N, W) > x) --w;
+  while (w + 1 < W && range_start(w + 1, N, W) <= x) ++w;
+  return w;
 }
 __device__ __forceinline__ long long readlane_i64(long long x, int src) {
   const int lo = __builtin_amdgcn_readlane((int)(unsigned)(x & 0xffffffffLL), src);
@@ -535,7 +552,7 @@ __global__ __launch_bounds__(64) void row_attn_kernel(RowAttnArgs a) {
     const long long N = total_steps(a, U, lane, first, nmax);
     const int W = balanced_waves(a.balance_pieces, N, nmax);
     if (w >= W) return;
-    const long long s_lo = (long long)w * N / W, s_hi = (long long)(w + 1) * N / W;
+    const long long s_lo = range_start(w, N, W), s_hi = range_start(w + 1, N, W);
     int b, L, start;
     long long base;
     if (!sequence_of_step(a, U, s_lo, lane, first, b, base, L, start)) return;
