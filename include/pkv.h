@@ -139,12 +139,13 @@ int pkv_rope_kv_store(void* q, const void* k, const void* v, const int32_t* posi
  * A sequence that fits one split has its output written by the first pass.
  *
  * split_tokens = PKV_SPLIT_BALANCED instead cuts the batch's context, taken
- * as steps of a few tokens sequence after sequence, into up to 1024 ranges of
- * equal size (one wave each per group of KV heads; each range at least 16
- * steps, and no sequence in more than 512 ranges), chosen on the device from
- * context_lens, so that the waves of the first pass carry equal work however
- * the context lengths are mixed.  A range may end inside one sequence and
- * cover the start of the next.
+ * as steps of a few tokens sequence after sequence, into up to 1024 nearly
+ * equal ranges (one wave each per group of KV heads; each range at least 16
+ * steps, and no sequence in more than 512 ranges; the waves that run on the
+ * odd-numbered dies, which stream slower, take 1/16 less), chosen on the
+ * device from context_lens, so that the waves of the first pass finish
+ * together however the context lengths are mixed.  A range may end inside
+ * one sequence and cover the start of the next.
  *
  * pkv_decode_split_tokens returns the split the library picks for a shape
  * (PKV_SPLIT_BALANCED when max_context_len > 256, else max_context_len

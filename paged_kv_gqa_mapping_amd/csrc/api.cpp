@@ -87,9 +87,10 @@ int32_t auto_split(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_l
 
 // Token-balanced decode (split_tokens = PKV_SPLIT_BALANCED): the batch's
 // steps (U tokens each), sequence after sequence, are cut into kBalancePieces
-// ranges of equal size, one wave each per group of KV heads, so that the
-// waves of a launch carry equal work whatever the mix of context lengths; a
-// multiple of the 256 compute units, so that each unit holds as many waves.
+// nearly equal ranges (row_attn.hpp), one wave each per group of KV heads, so
+// that the waves of a launch finish together whatever the mix of context
+// lengths; a multiple of the 256 compute units, so that each unit holds as
+// many waves.
 #ifndef PKV_BALANCE_PIECES
 #define PKV_BALANCE_PIECES 1024
 #endif

@@ -3,9 +3,10 @@
 //
 //  * Decode: a row is sequence b's new token.  Its context is cut into splits
 //    of split_tokens keys, one wave per (sequence, KV-head group, split), or
-//    (token-balanced) the batch's contexts are cut into equal ranges that may
-//    cross sequences, one wave per (range, KV-head group).  A part of a
-//    context writes an unnormalised softmax state that decode_reduce merges.
+//    (token-balanced) the batch's contexts are cut into nearly equal ranges
+//    that may cross sequences, one wave per (range, KV-head group).  A part
+//    of a context writes an unnormalised softmax state that decode_reduce
+//    merges.
 //  * Prefill rows (fp32 path): query i of sequence b attends keys 0..p with
 //    p = Lk - Lq + i, in one split.
 //
